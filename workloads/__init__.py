@@ -1,0 +1,111 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module holds NO arithmetic of the method: it only draws i.i.d. normal numbers,
+scales them and rounds them to the storage type.  Both the oracle and the HIP path
+consume what it returns; neither is imported here.
+
+Recipe (one per workload, fixed order Q, K, V, dO, U_Q, U_K, U_V):
+  numpy Generator(PCG64(seed)).standard_normal(shape, float32) per tensor,
+  shape (B, H, N, d); optional scaling of U_* or of Q, K; then, for bf16 workloads,
+  round-to-nearest-even to bfloat16 (values returned as float32 that are exactly
+  representable in bf16, so both sides see identical inputs).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TENSORS = ("Q", "K", "V", "dO", "UQ", "UK", "UV")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str              # "f32" or "bf16": storage type of the seven inputs
+    seed: int
+    scale_u: float = 1.0    # multiplies U_Q, U_K, U_V
+    scale_qk: float = 1.0   # multiplies Q and K
+    causal: bool = False
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def tau(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+# The five workloads of the benchmark plan: sizes, dtypes, scalings and masks.
+WORKLOADS = {
+    "single_head_n128_d64_f32": Workload(
+        "single_head_n128_d64_f32", B=1, H=1, N=128, d=64, dtype="f32", seed=1001,
+        note="single head, fp32 inputs"),
+    "gpt2_heads_h12_n4096_d64_bf16": Workload(
+        "gpt2_heads_h12_n4096_d64_bf16", B=1, H=12, N=4096, d=64, dtype="bf16", seed=1002,
+        note="GPT-2-style heads"),
+    "h12_n16384_d64_bf16_u01": Workload(
+        "h12_n16384_d64_bf16_u01", B=1, H=12, N=16384, d=64, dtype="bf16", seed=1003,
+        scale_u=0.1, note="U_Q, U_K, U_V scaled by 0.1; headline timing workload"),
+    "h8_n65536_d128_bf16_qk2": Workload(
+        "h8_n65536_d128_bf16_qk2", B=1, H=8, N=65536, d=128, dtype="bf16", seed=1004,
+        scale_qk=2.0, note="Q and K scaled by 2: sharp softmax rows"),
+    "h1_n262144_d64_bf16": Workload(
+        "h1_n262144_d64_bf16", B=1, H=1, N=262144, d=64, dtype="bf16", seed=1005,
+        note="long-context single head"),
+}
+
+HEADLINE = "h12_n16384_d64_bf16_u01"
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); return float32.
+
+    Bit-level: add 0x7FFF plus the lowest kept bit, then clear the low 16 bits.
+    Inputs here are finite normals, so NaN/Inf handling is not needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def make_inputs(w: Workload, heads=None) -> dict:
+    """Draw the seven input tensors of workload ``w`` as float32 arrays (B, H, N, d).
+
+    ``heads``: optional list of flat (b*H + h) head indices to keep; the full draw is
+    still made in the fixed order so that every head's values do not depend on which
+    heads are requested.
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    shape = (w.B, w.H, w.N, w.d)
+    out = {}
+    for name in TENSORS:
+        t = rng.standard_normal(shape, dtype=np.float32)
+        if name in ("UQ", "UK", "UV") and w.scale_u != 1.0:
+            t *= np.float32(w.scale_u)
+        if name in ("Q", "K") and w.scale_qk != 1.0:
+            t *= np.float32(w.scale_qk)
+        if w.dtype == "bf16":
+            t = round_to_bf16(t)
+        if heads is not None:
+            t = t.reshape(w.B * w.H, w.N, w.d)[list(heads)]
+        out[name] = t
+    return out
+
+
+def small(name: str, B: int, H: int, N: int, d: int, dtype: str, seed: int,
+          **kw) -> Workload:
+    """An ad-hoc workload with the same recipe (used for edge-case and tail tests)."""
+    return Workload(name, B=B, H=H, N=N, d=d, dtype=dtype, seed=seed, **kw)
