@@ -1,0 +1,180 @@
+"""Exact backward-over-backward (BoB) of softmax attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/fbob.h`` (``libfbob.so``, built
+in-tree by ``exact_softmax_attention_fbob_amd.build``).  This module only
+marshals arguments: it checks shapes, dtypes, devices and contiguity, allocates
+the output tensors with torch (device memory) and passes raw pointers and
+torch's current HIP stream to the library.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback path.
+
+Entry points (same names as the C ABI):
+    forward(Q, K, V, dO, tau, causal)              -> O, L, D
+    bob(Q, K, V, dO, UQ, UK, UV, O, L, D, ...)     -> dict(dQt, dKt, dVt, ddOt, alpha, E)
+    bob_pass1(...)                                  -> dict(dQt, ddOt, alpha, E)
+    bob_pass2(..., alpha, E)                        -> dict(dKt, dVt)
+Shapes: Q, dO, U_Q: [B, Hq, N, d]; K, V, U_K, U_V: [B, Hkv, N, d]; L, D, alpha,
+E: [B, Hq, N]; all outputs float32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from ._lib import FbobError, load_library, STATUS  # noqa: F401
+
+__all__ = ["forward", "bob", "bob_pass1", "bob_pass2", "load_library", "FbobError",
+           "library_path", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfbob.so")
+
+
+def version() -> int:
+    return load_library().fbob_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return 1
+    if t.dtype == torch.float32:
+        return 0
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_inputs(Q, K, V, dO, UQ=None, UK=None, UV=None):
+    ins = [x for x in (Q, K, V, dO, UQ, UK, UV) if x is not None]
+    for x in ins:
+        if not x.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not x.is_contiguous():
+            raise ValueError("all tensors must be contiguous ([B, H, N, d], d fastest)")
+        if x.dtype != Q.dtype:
+            raise TypeError("the seven inputs must share one dtype")
+        if x.dim() != 4:
+            raise ValueError("inputs are 4-D [B, H, N, d]")
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    for x in (Q, dO, UQ):
+        if x is not None and tuple(x.shape) != (B, Hq, N, d):
+            raise ValueError(f"expected query-side shape {(B, Hq, N, d)}, got {tuple(x.shape)}")
+    for x in (K, V, UK, UV):
+        if x is not None and tuple(x.shape) != (B, Hkv, N, d):
+            raise ValueError(f"expected key-side shape {(B, Hkv, N, d)}, got {tuple(x.shape)}")
+    return B, Hq, Hkv, N, d
+
+
+def _check_f32(x, shape, name):
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _call(fn, *args):
+    st = fn(*args)
+    if st != 0:
+        raise FbobError(st)
+
+
+def _tau(tau, d):
+    return ctypes.c_float(1.0 / math.sqrt(d) if tau is None else float(tau))
+
+
+def forward(Q, K, V, dO, tau=None, causal=False):
+    """O, L, D for the BoB row state (C ABI ``fbob_forward``)."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO)
+    O = torch.empty((B, Hq, N, d), dtype=torch.float32, device=Q.device)
+    L = torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
+    D = torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
+    _call(lib.fbob_forward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+          _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L), _p(D), _stream())
+    return O, L, D
+
+
+def _row_state(O, L, D, B, Hq, N, d):
+    _check_f32(O, (B, Hq, N, d), "O")
+    _check_f32(L, (B, Hq, N), "L")
+    _check_f32(D, (B, Hq, N), "D")
+
+
+def bob(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, out=None):
+    """Exact BoB outputs (C ABI ``fbob_bob``: Pass 1 then Pass 2 on one stream).
+
+    ``out`` may supply preallocated float32 outputs (dict with the six keys).
+    """
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
+    _row_state(O, L, D, B, Hq, N, d)
+    if out is None:
+        dev = Q.device
+        out = dict(dQt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+                   dKt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+                   dVt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+                   ddOt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+                   alpha=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+                   E=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    else:
+        for k, shp in (("dQt", (B, Hq, N, d)), ("dKt", (B, Hkv, N, d)), ("dVt", (B, Hkv, N, d)),
+                       ("ddOt", (B, Hq, N, d)), ("alpha", (B, Hq, N)), ("E", (B, Hq, N))):
+            _check_f32(out[k], shp, k)
+    _call(lib.fbob_bob, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+          _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
+          _p(out["dQt"]), _p(out["dKt"]), _p(out["dVt"]), _p(out["ddOt"]),
+          _p(out["alpha"]), _p(out["E"]), _stream())
+    return out
+
+
+def bob_pass1(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False):
+    """Pass 1 alone (C ABI ``fbob_bob_pass1``): dQt, ddOt, alpha, E."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
+    _row_state(O, L, D, B, Hq, N, d)
+    dev = Q.device
+    out = dict(dQt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               ddOt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               alpha=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+               E=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    _call(lib.fbob_bob_pass1, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+          _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
+          _p(out["dQt"]), _p(out["ddOt"]), _p(out["alpha"]), _p(out["E"]), _stream())
+    return out
+
+
+def bob_pass2(Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, tau=None, causal=False):
+    """Pass 2 alone (C ABI ``fbob_bob_pass2``): dKt, dVt."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
+    for x, name in ((L, "L"), (D, "D"), (alpha, "alpha"), (E, "E")):
+        _check_f32(x, (B, Hq, N), name)
+    dev = Q.device
+    out = dict(dKt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               dVt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev))
+    _call(lib.fbob_bob_pass2, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+          _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(L), _p(D), _p(alpha), _p(E),
+          _p(out["dKt"]), _p(out["dVt"]), _stream())
+    return out

@@ -1,0 +1,59 @@
+"""ctypes loader for ``libfbob.so`` with the prototypes of ``include/fbob.h``.
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+STATUS = {0: "FBOB_OK", 1: "FBOB_ERR_INVALID_ARG", 2: "FBOB_ERR_UNSUPPORTED",
+          3: "FBOB_ERR_ALIGNMENT", 4: "FBOB_ERR_ALIAS", 5: "FBOB_ERR_HIP"}
+
+# Every symbol declared in include/fbob.h, with its ctypes prototype.
+_i64, _f, _i, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
+_SIZES = [_i, _i64, _i64, _i64, _i64, _i64, _f, _i]  # dtype, B, Hq, Hkv, N, d, tau, causal
+PROTOTYPES = {
+    "fbob_forward": (_i, _SIZES + [_vp] * 4 + [_vp] * 3 + [_vp]),
+    "fbob_bob": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp]),
+    "fbob_bob_pass1": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 4 + [_vp]),
+    "fbob_bob_pass2": (_i, _SIZES + [_vp] * 7 + [_vp] * 4 + [_vp] * 2 + [_vp]),
+    "fbob_strerror": (ctypes.c_char_p, [_i]),
+    "fbob_version": (_i, []),
+}
+
+
+class FbobError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = STATUS.get(status, f"status {status}")
+        try:
+            msg += ": " + load_library().fbob_strerror(status).decode()
+        except Exception:  # pragma: no cover - message only
+            pass
+        super().__init__(msg)
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle of libfbob.so."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or os.path.join(_HERE, "libfbob.so")
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build the HIP library first "
+            "(python -m exact_softmax_attention_fbob_amd.build)")
+    lib = ctypes.CDLL(p)
+    for name, (res, argt) in PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = argt
+    if path is None:
+        _LIB = lib
+    return lib

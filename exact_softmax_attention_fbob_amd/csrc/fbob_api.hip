@@ -1,0 +1,184 @@
+// fbob_api.hip - the C ABI declared in include/fbob.h: argument validation,
+// dispatch on (dtype, d, causal) and kernel launch.  Validation happens before
+// any HIP call so that every error path is testable on a host without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fbob.h"
+#include "fbob_launch.hpp"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(const Range& x, const Range& y) { return x.lo < y.hi && y.lo < x.hi; }
+
+struct Checked {
+  int status;
+  fbob::Problem p;
+  bool empty;
+};
+
+// Shared size/dtype checks.  int32 per-head indexing: N * d must fit in int32 and
+// every work-group index must fit in int32.
+Checked check_sizes(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    float tau, int causal) {
+  Checked c{FBOB_OK, {}, false};
+  if (dtype != FBOB_DTYPE_F32 && dtype != FBOB_DTYPE_BF16) return {FBOB_ERR_INVALID_ARG, {}, false};
+  if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return {FBOB_ERR_INVALID_ARG, {}, false};
+  if (!(tau > 0.f) || !isfinite(tau)) return {FBOB_ERR_INVALID_ARG, {}, false};
+  if (d != 64 && d != 128) return {FBOB_ERR_UNSUPPORTED, {}, false};
+  if (B == 0 || Hq == 0 || N == 0) {
+    if (Hkv < 0 || (Hkv == 0 && Hq != 0)) return {FBOB_ERR_INVALID_ARG, {}, false};
+    c.empty = true;
+  } else {
+    if (Hkv == 0 || Hq % Hkv != 0) return {FBOB_ERR_INVALID_ARG, {}, false};
+  }
+  if (N > (int64_t)INT32_MAX / d) return {FBOB_ERR_UNSUPPORTED, {}, false};
+  if (B * Hq > (int64_t)INT32_MAX / 64 || (N / 64 + 1) * B * Hq > (int64_t)INT32_MAX)
+    return {FBOB_ERR_UNSUPPORTED, {}, false};
+  c.p.B = (int)B;
+  c.p.Hq = (int)Hq;
+  c.p.Hkv = (int)(Hkv == 0 ? 1 : Hkv);
+  c.p.N = (int)N;
+  c.p.d = (int)d;
+  c.p.tau = tau;
+  c.p.causal = causal ? 1 : 0;
+  c.p.bf16 = dtype == FBOB_DTYPE_BF16;
+  return c;
+}
+
+// Pointer checks: non-NULL, 16-byte aligned, outputs disjoint from every other
+// buffer.  `ins`/`outs` carry (pointer, byte size).
+int check_ptrs(const void* const* ins, const int64_t* in_bytes, int n_in, void* const* outs,
+               const int64_t* out_bytes, int n_out) {
+  for (int k = 0; k < n_in; ++k)
+    if (ins[k] == nullptr) return FBOB_ERR_INVALID_ARG;
+  for (int k = 0; k < n_out; ++k)
+    if (outs[k] == nullptr) return FBOB_ERR_INVALID_ARG;
+  for (int k = 0; k < n_in; ++k)
+    if (reinterpret_cast<uintptr_t>(ins[k]) % 16) return FBOB_ERR_ALIGNMENT;
+  for (int k = 0; k < n_out; ++k)
+    if (reinterpret_cast<uintptr_t>(outs[k]) % 16) return FBOB_ERR_ALIGNMENT;
+  for (int k = 0; k < n_out; ++k) {
+    const Range o = span(outs[k], out_bytes[k]);
+    for (int m = 0; m < n_in; ++m)
+      if (overlap(o, span(ins[m], in_bytes[m]))) return FBOB_ERR_ALIAS;
+    for (int m = k + 1; m < n_out; ++m)
+      if (overlap(o, span(outs[m], out_bytes[m]))) return FBOB_ERR_ALIAS;
+  }
+  return FBOB_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? FBOB_OK : FBOB_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fbob_version(void) { return FBOB_VERSION; }
+
+const char* fbob_strerror(int status) {
+  switch (status) {
+    case FBOB_OK: return "ok";
+    case FBOB_ERR_INVALID_ARG: return "invalid argument";
+    case FBOB_ERR_UNSUPPORTED: return "unsupported size or head dimension";
+    case FBOB_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case FBOB_ERR_ALIAS: return "output buffer overlaps another buffer";
+    case FBOB_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+                 int causal, const void* Q, const void* K, const void* V, const void* dO,
+                 float* O, float* L, float* D, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (c.empty) return FBOB_OK;
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO};
+  const int64_t inb[] = {qb, kb, kb, qb};
+  void* outs[] = {O, L, D};
+  const int64_t outb[] = {ob, rb, rb};
+  const int st = check_ptrs(ins, inb, 4, outs, outb, 3);
+  if (st != FBOB_OK) return st;
+  fbob::FwdArgs a{Q, K, V, dO, O, L, D};
+  return finish(fbob::launch_forward(c.p, a, static_cast<hipStream_t>(stream)));
+}
+
+int fbob_bob_pass1(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+                   int causal, const void* Q, const void* K, const void* V, const void* dO,
+                   const void* UQ, const void* UK, const void* UV, const float* O, const float* L,
+                   const float* D, float* dQt, float* ddOt, float* alpha, float* E, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (c.empty) return FBOB_OK;
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, O, L, D};
+  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, ob, rb, rb};
+  void* outs[] = {dQt, ddOt, alpha, E};
+  const int64_t outb[] = {ob, ob, rb, rb};
+  const int st = check_ptrs(ins, inb, 10, outs, outb, 4);
+  if (st != FBOB_OK) return st;
+  fbob::Pass1Args a{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E};
+  return finish(fbob::launch_pass1(c.p, a, static_cast<hipStream_t>(stream)));
+}
+
+int fbob_bob_pass2(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+                   int causal, const void* Q, const void* K, const void* V, const void* dO,
+                   const void* UQ, const void* UK, const void* UV, const float* L, const float* D,
+                   const float* alpha, const float* E, float* dKt, float* dVt, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (c.empty) return FBOB_OK;
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, L, D, alpha, E};
+  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, rb, rb, rb, rb};
+  void* outs[] = {dKt, dVt};
+  const int64_t outb[] = {kob, kob};
+  const int st = check_ptrs(ins, inb, 11, outs, outb, 2);
+  if (st != FBOB_OK) return st;
+  fbob::Pass2Args a{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
+  return finish(fbob::launch_pass2(c.p, a, static_cast<hipStream_t>(stream)));
+}
+
+int fbob_bob(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+             int causal, const void* Q, const void* K, const void* V, const void* dO,
+             const void* UQ, const void* UK, const void* UV, const float* O, const float* L,
+             const float* D, float* dQt, float* dKt, float* dVt, float* ddOt, float* alpha,
+             float* E, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (c.empty) return FBOB_OK;
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, O, L, D};
+  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, ob, rb, rb};
+  void* outs[] = {dQt, dKt, dVt, ddOt, alpha, E};
+  const int64_t outb[] = {ob, kob, kob, ob, rb, rb};
+  const int st = check_ptrs(ins, inb, 10, outs, outb, 6);
+  if (st != FBOB_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  fbob::Pass1Args a1{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E};
+  hipError_t e = fbob::launch_pass1(c.p, a1, s);
+  if (e != hipSuccess) return FBOB_ERR_HIP;
+  fbob::Pass2Args a2{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
+  return finish(fbob::launch_pass2(c.p, a2, s));
+}
+
+}  // extern "C"

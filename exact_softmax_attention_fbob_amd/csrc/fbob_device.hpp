@@ -1,0 +1,231 @@
+// fbob_device.hpp - gfx950 device primitives shared by the forward, Pass 1 and
+// Pass 2 kernels: MFMA fragments, LDS tile layout, tile staging, lane reductions.
+//
+// Wavefront layout used everywhere (64 lanes, lane = 16 g + r, r in [0,16),
+// g in [0,4)), for a 16x16 output block of a 16x16xK MFMA:
+//   A operand  lane (r, g) holds A[row r][k(g, e)], e = 0..7
+//   B operand  lane (r, g) holds B[k(g, e)][col r]
+//   C/D        lane (r, g) holds C[row 4 g + q][col r], q = 0..3
+// Only the pairing of (g, e) between A and B matters for the product, so any
+// bijection k(g, e) works as long as both operands use the same one.  The score
+// tiles are computed transposed (keys/rows that are contracted later along the
+// C "row" axis) so that the C registers of two adjacent 16-row blocks are directly
+// the 8-element B operand of the next contraction, with
+//   k(g, e) = 16 (e / 4) + 4 g + (e % 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fbob {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Element traits: storage type of the seven inputs.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<__bf16> {
+  using frag = bf16x8;  // 8 operand elements per lane
+  static __device__ __forceinline__ frag from_f32(const f32x4 lo, const f32x4 hi) {
+    frag o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[q] = (__bf16)lo[q];
+      o[4 + q] = (__bf16)hi[q];
+    }
+    return o;
+  }
+  // C += A * B for one 16x16x32 block (bf16 inputs, fp32 accumulate).
+  static __device__ __forceinline__ f32x4 mma(const frag a, const frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Elem<float> {
+  using frag = f32x8;
+  static __device__ __forceinline__ frag from_f32(const f32x4 lo, const f32x4 hi) {
+    frag o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[q] = lo[q];
+      o[4 + q] = hi[q];
+    }
+    return o;
+  }
+  // Same contraction as the bf16 block: eight fp32 16x16x4 MFMAs, the e-th one
+  // pairing element e of every lane (k index g within that MFMA).
+  static __device__ __forceinline__ f32x4 mma(const frag a, const frag b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// LDS tile: R rows x D columns of T, row-major, 16-byte chunks XOR-swizzled
+// within a row so that (a) eight consecutive rows read at one column chunk and
+// (b) the 4-row x 32-byte pattern of a transposed read both hit distinct banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+template <typename T, int D>
+struct Tile {
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row
+  static_assert(kChunks >= 8, "swizzle needs at least 8 chunks per row");
+  // byte offset of chunk c of row `row`
+  static __device__ __forceinline__ int chunk_off(int row, int c) {
+    return row * kRowBytes + ((c ^ swz(row)) << 4);
+  }
+  // byte offset of element (row, col)
+  static __device__ __forceinline__ int elem_off(int row, int col) {
+    constexpr int per_chunk = 16 / (int)sizeof(T);
+    return chunk_off(row, col / per_chunk) + (col % per_chunk) * (int)sizeof(T);
+  }
+};
+
+// Row-major operand fragment: 8 consecutive elements (row, col .. col+7),
+// col a multiple of 8.
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag lds_frag_row(const char* tile, int row, int col) {
+  using F = typename Elem<T>::frag;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const F*>(tile + Tile<T, D>::chunk_off(row, col >> 3));
+  } else {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::chunk_off(row, col >> 2));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::chunk_off(row, (col >> 2) + 1));
+    return Elem<T>::from_f32(lo, hi);
+  }
+}
+
+// Transposed operand fragment for a contraction over tile rows: lane (r, g)
+// gets X[row0 + k(g, e)][col0 + r], k(g, e) = 16 (e / 4) + 4 g + (e % 4).
+// bf16 uses the gfx950 transposing LDS read: in each 16-lane group, lane
+// (4 b + c) addresses 4 elements of row b at columns 4c..4c+3 and receives
+// column r of the 4 addressed rows.
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag lds_frag_tr(const char* tile, int row0, int col0,
+                                                              int r, int g) {
+  using F = typename Elem<T>::frag;
+  if constexpr (sizeof(T) == 2) {
+#if FBOB_NO_TR_READ
+    F o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = row0 + 16 * (e >> 2) + 4 * g + (e & 3);
+      o[e] = *reinterpret_cast<const __bf16*>(tile + Tile<T, D>::elem_off(row, col0 + r));
+    }
+    return o;
+#else
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int b = r >> 2, c = r & 3;
+    const int off0 = Tile<T, D>::elem_off(row0 + 4 * g + b, col0 + 4 * c);
+    const int off1 = Tile<T, D>::elem_off(row0 + 16 + 4 * g + b, col0 + 4 * c);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(reinterpret_cast<uintptr_t>(tile) + off0));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(reinterpret_cast<uintptr_t>(tile) + off1));
+    F o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[q] = lo[q];
+      o[4 + q] = hi[q];
+    }
+    return o;
+#endif
+  } else {
+    F o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = row0 + 16 * (e >> 2) + 4 * g + (e & 3);
+      o[e] = *reinterpret_cast<const float*>(tile + Tile<T, D>::elem_off(row, col0 + r));
+    }
+    return o;
+  }
+}
+
+// Operand fragment straight from global memory: 8 consecutive elements of one
+// row, or zeros when the row is past the end.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag global_frag(const T* base, int row, int nrows,
+                                                              int ld, int col) {
+  using F = typename Elem<T>::frag;
+  F o;
+  if (row < nrows) {
+    o = *reinterpret_cast<const F*>(base + (int64_t)row * ld + col);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (T)0.0f;
+  }
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// Tile staging: global (rows row0.., D columns, contiguous) -> registers -> LDS.
+// Rows at or past `nrows` are zero-filled.  kPer = 16-byte chunks per thread.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int ROWS, int NTHREADS>
+struct Stager {
+  static constexpr int kChunks = Tile<T, D>::kChunks;
+  static constexpr int kTotal = ROWS * kChunks;
+  static_assert(kTotal % NTHREADS == 0, "tile chunks must divide evenly over threads");
+  static constexpr int kPer = kTotal / NTHREADS;
+  u32x4 v[kPer];
+
+  __device__ __forceinline__ void load(const T* src, int row0, int nrows, int tid) {
+    const char* s = reinterpret_cast<const char*>(src);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = tid + k * NTHREADS;
+      const int row = idx / kChunks, c = idx % kChunks;
+      if (row0 + row < nrows) {
+        v[k] = *reinterpret_cast<const u32x4*>(s + (int64_t)(row0 + row) * Tile<T, D>::kRowBytes + c * 16);
+      } else {
+        v[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, int tid) const {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = tid + k * NTHREADS;
+      const int row = idx / kChunks, c = idx % kChunks;
+      *reinterpret_cast<u32x4*>(tile + Tile<T, D>::chunk_off(row, c)) = v[k];
+    }
+  }
+};
+
+// Sum over the four 16-lane groups (lanes r, r+16, r+32, r+48).
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work-group index remapped so that consecutive logical blocks run on the same
+// XCD (the dispatcher hands block b to XCD b % 8): blocks of one head then share
+// that XCD's L2 for the streamed operand tiles.  Bijective for any `total`.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, rem = total % kXcd;
+  const int xcd = bid % kXcd, slot = bid / kXcd;
+  return (xcd < rem) ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+}
+
+}  // namespace fbob

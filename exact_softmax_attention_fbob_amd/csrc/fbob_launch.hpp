@@ -1,0 +1,39 @@
+// fbob_launch.hpp - internal interface between the C ABI (fbob_api.hip) and the
+// kernel translation units.  Sizes are already validated; pointers are device
+// pointers; all launches go to `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fbob {
+
+struct Problem {
+  int B, Hq, Hkv, N, d;
+  float tau;
+  int causal;
+  bool bf16;  // storage type of the seven inputs (else fp32)
+};
+
+struct FwdArgs {
+  const void *Q, *K, *V, *dO;
+  float *O, *L, *D;
+};
+
+struct Pass1Args {
+  const void *Q, *K, *V, *dO, *UQ, *UK, *UV;
+  const float *O, *L, *D;
+  float *dQt, *ddOt, *alpha, *E;
+};
+
+struct Pass2Args {
+  const void *Q, *K, *V, *dO, *UQ, *UK, *UV;
+  const float *L, *D, *alpha, *E;
+  float *dKt, *dVt;
+};
+
+hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
+hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s);
+hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s);
+
+}  // namespace fbob

@@ -1,0 +1,140 @@
+/*
+ * fbob.h - C ABI of the MI355X (gfx950) library for exact backward-over-backward
+ * (BoB) of softmax attention.
+ *
+ * Method: "FlashBoB: I/O-Efficient Exact Backward-over-Backward for Softmax
+ * Attention" (papernotes.org notes and abstract).  For one attention head with
+ * S = tau Q K^T, P = softmax_row(S), O = P V and upstream gradient dO, the first
+ * backward gives dQ, dK, dV ("FlashAttention 的反向传播设计", section 一).  BoB
+ * differentiates the scalar
+ *        Phi = <dQ, U_Q> + <dK, U_K> + <dV, U_V>
+ * with respect to (Q, K, V, dO) and returns (dQ~, dK~, dV~, ddO~) plus the two
+ * row scalars alpha_i = sum_j P_ij F_ij (F = tau (U_Q K^T + Q U_K^T)) and
+ * E_i = sum_j P_ij dP~_ij (FlashBoB notes, "整体框架" and "关键设计" item 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.
+ *  * Shapes: per-query-head tensors are [B, Hq, N, d] and per-key/value-head
+ *    tensors are [B, Hkv, N, d], contiguous, d fastest.  Row vectors (L, D,
+ *    alpha, E) are [B, Hq, N].  Hq must be a multiple of Hkv (grouped-query
+ *    attention shares one K/V head among Hq/Hkv consecutive query heads).
+ *  * dtype (fbob_dtype) is the storage type of the seven inputs Q, K, V, dO,
+ *    U_Q, U_K, U_V.  O, L, D and every output are float32.  Arithmetic: bf16
+ *    inputs use bf16 x bf16 -> fp32 MFMA; f32 inputs use fp32 MFMA; exp and all
+ *    row scalars are fp32.
+ *  * tau is the score scale (S = tau Q K^T); L is the natural-log log-sum-exp
+ *    of the scaled scores of each row.
+ *  * causal != 0 masks key positions j > i (P_ij = 0).
+ *  * d must be 64 or 128.  N may be any value >= 0 (ragged tails are masked).
+ *    B, Hq, Hkv or N equal to 0 is an empty problem: FBOB_OK, nothing written.
+ *  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Every output element is written exactly once (no atomics, no
+ *    accumulate-into), so outputs need no initialisation.  Calls are reentrant.
+ *  * Errors: arguments are validated before any HIP call and reported by the
+ *    return value; the library never aborts, throws or prints.
+ *      FBOB_ERR_INVALID_ARG  negative size, NULL pointer, bad dtype, Hq % Hkv,
+ *                            non-finite or non-positive tau
+ *      FBOB_ERR_UNSUPPORTED  d not 64 or 128, or a size that overflows int32
+ *                            per-head indexing
+ *      FBOB_ERR_ALIGNMENT    a pointer not 16-byte aligned
+ *      FBOB_ERR_ALIAS        an output range overlaps an input or another output
+ *      FBOB_ERR_HIP          a HIP launch error (hipGetLastError after launch)
+ */
+#ifndef FBOB_H_
+#define FBOB_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FBOB_VERSION 1
+
+typedef enum {
+  FBOB_OK = 0,
+  FBOB_ERR_INVALID_ARG = 1,
+  FBOB_ERR_UNSUPPORTED = 2,
+  FBOB_ERR_ALIGNMENT = 3,
+  FBOB_ERR_ALIAS = 4,
+  FBOB_ERR_HIP = 5
+} fbob_status;
+
+typedef enum { FBOB_DTYPE_F32 = 0, FBOB_DTYPE_BF16 = 1 } fbob_dtype;
+
+/*
+ * Forward pass with the row state that BoB recomputes from.
+ * FlashAttention blog, section 一 (S, P, O) and section 二 (keep per-row
+ * statistics instead of P); FlashBoB notes, "关键设计" 1 (D_i = do_i^T o_i) and
+ * "关键设计" 2 (P is rebuilt on chip from the stored log-partition L).
+ *
+ *   in : Q [B,Hq,N,d], K, V [B,Hkv,N,d], dO [B,Hq,N,d]   (dtype)
+ *   out: O [B,Hq,N,d] = P V (fp32)
+ *        L [B,Hq,N]   = log sum_j exp(tau Q_i . K_j)     (fp32, natural log)
+ *        D [B,Hq,N]   = dO_i . O_i                        (fp32, from fp32 O)
+ */
+int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                 float tau, int causal,
+                 const void* Q, const void* K, const void* V, const void* dO,
+                 float* O, float* L, float* D, void* stream);
+
+/*
+ * Exact BoB: Pass 1 then Pass 2 on the same stream (FlashBoB notes,
+ * "整体框架" flowchart and "关键设计" 2).  No N x N tensor is written to memory;
+ * alpha and E are the only state that crosses from Pass 1 to Pass 2.
+ *
+ *   in : Q, K, V, dO, U_Q [B,Hq,N,d], U_K, U_V [B,Hkv,N,d] (dtype)
+ *        O, L, D from fbob_forward on the same (Q, K, V, dO, tau, causal);
+ *        anything else gives undefined (but memory-safe) results.
+ *   out: dQt, ddOt [B,Hq,N,d]; dKt, dVt [B,Hkv,N,d]; alpha, E [B,Hq,N]  (fp32)
+ */
+int fbob_bob(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+             float tau, int causal,
+             const void* Q, const void* K, const void* V, const void* dO,
+             const void* UQ, const void* UK, const void* UV,
+             const float* O, const float* L, const float* D,
+             float* dQt, float* dKt, float* dVt, float* ddOt,
+             float* alpha, float* E, void* stream);
+
+/*
+ * Pass 1 alone (row-resident; FlashBoB notes, "关键设计" 2, first pass): streams
+ * K, V, U_K, U_V column tiles past a resident row block, accumulates alpha and the
+ * five alpha-free accumulators, applies the affine correction of "关键设计" 1
+ *   E = E' - alpha D,  ddO~ = ddO~' - alpha o,  dQ~ = tau (Omega - alpha R - E B)
+ * and writes dQt, ddOt, alpha, E once.  Same arguments as fbob_bob minus dKt, dVt.
+ */
+int fbob_bob_pass1(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                   float tau, int causal,
+                   const void* Q, const void* K, const void* V, const void* dO,
+                   const void* UQ, const void* UK, const void* UV,
+                   const float* O, const float* L, const float* D,
+                   float* dQt, float* ddOt, float* alpha, float* E, void* stream);
+
+/*
+ * Pass 2 alone (column-resident; FlashBoB notes, "关键设计" 2, second pass and
+ * "关键设计" 3 for the grouped heads): streams row tiles of Q, dO, U_Q, L, D and
+ * the Pass 1 scalars (alpha, E) past a resident K/V column block, and writes
+ * dKt, dVt exactly once (the query heads of a group are summed on chip).
+ *   in : as fbob_bob, plus alpha, E from fbob_bob_pass1 on the same inputs.
+ *   out: dKt, dVt [B,Hkv,N,d] (fp32)
+ */
+int fbob_bob_pass2(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                   float tau, int causal,
+                   const void* Q, const void* K, const void* V, const void* dO,
+                   const void* UQ, const void* UK, const void* UV,
+                   const float* L, const float* D, const float* alpha, const float* E,
+                   float* dKt, float* dVt, void* stream);
+
+/* Static string naming a status code ("unknown status" for other values). */
+const char* fbob_strerror(int status);
+
+/* FBOB_VERSION of the built library. */
+int fbob_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FBOB_H_ */

@@ -1,0 +1,133 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+* the library loads and exports every function declared in include/fbob.h;
+* argument validation returns the documented status before any HIP call.
+Pointers passed here are fake addresses: every call below is rejected (or is an
+empty problem) before anything dereferences them.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_softmax_attention_fbob_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fbob.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, ALIAS = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fbob_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(os.path.join(ROOT, "exact_softmax_attention_fbob_amd", "libfbob.so")):
+        pytest.skip("libfbob.so not built (run __graft_entry__.build())")
+    return _lib.load_library()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(
+        ["fbob_forward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2", "fbob_strerror",
+         "fbob_version"])
+    assert sorted(_lib.PROTOTYPES) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.fbob_version() == 1
+    for st in range(6):
+        assert lib.fbob_strerror(st)
+    assert lib.fbob_strerror(99) == b"unknown status"
+
+
+class FakeBuffers:
+    """Disjoint, 16-byte aligned fake device addresses for every argument."""
+
+    def __init__(self, n, stride=1 << 32):
+        self.addrs = [0x100000000000 + k * stride for k in range(n)]
+
+    def __getitem__(self, k):
+        return ctypes.c_void_p(self.addrs[k])
+
+
+def call_bob(lib, dtype=1, B=1, Hq=2, Hkv=2, N=64, d=64, tau=0.125, causal=0, ptrs=None):
+    p = ptrs or [FakeBuffers(16)[k] for k in range(16)]
+    return lib.fbob_bob(dtype, B, Hq, Hkv, N, d, ctypes.c_float(tau), causal, *p[:16],
+                        ctypes.c_void_p(0))
+
+
+def call_forward(lib, dtype=1, B=1, Hq=2, Hkv=2, N=64, d=64, tau=0.125, ptrs=None):
+    p = ptrs or [FakeBuffers(7)[k] for k in range(7)]
+    return lib.fbob_forward(dtype, B, Hq, Hkv, N, d, ctypes.c_float(tau), 0, *p[:7],
+                            ctypes.c_void_p(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(dtype=7), INVALID), (dict(N=-1), INVALID), (dict(B=-2), INVALID),
+    (dict(Hq=3, Hkv=2), INVALID), (dict(Hkv=0), INVALID), (dict(tau=0.0), INVALID),
+    (dict(tau=float("nan")), INVALID), (dict(tau=-1.0), INVALID),
+    (dict(N=0), OK), (dict(B=0), OK), (dict(Hq=0, Hkv=0), OK),
+    (dict(N=(1 << 31) // 64 + 1), UNSUPPORTED),
+])
+def test_size_validation(lib, kw, status):
+    assert call_bob(lib, **kw) == status
+    fkw = {k: v for k, v in kw.items() if k != "causal"}
+    assert call_forward(lib, **fkw) == status
+
+
+def test_null_pointer_is_invalid(lib):
+    fb = FakeBuffers(16)
+    for k in range(16):
+        ptrs = [fb[m] for m in range(16)]
+        ptrs[k] = ctypes.c_void_p(0)
+        assert call_bob(lib, ptrs=ptrs) == INVALID, k
+
+
+def test_misaligned_pointer(lib):
+    fb = FakeBuffers(16)
+    for k in range(16):
+        ptrs = [fb[m] for m in range(16)]
+        ptrs[k] = ctypes.c_void_p(fb.addrs[k] + 8)
+        assert call_bob(lib, ptrs=ptrs) == ALIGN, k
+
+
+def test_output_aliasing_an_input_or_another_output(lib):
+    fb = FakeBuffers(16)
+    # output dQt (index 10) placed inside input K (index 1)
+    ptrs = [fb[m] for m in range(16)]
+    ptrs[10] = ctypes.c_void_p(fb.addrs[1] + 16 * 64)
+    assert call_bob(lib, ptrs=ptrs) == ALIAS
+    # alpha (14) overlapping E (15)
+    ptrs = [fb[m] for m in range(16)]
+    ptrs[15] = ctypes.c_void_p(fb.addrs[14] + 16)
+    assert call_bob(lib, ptrs=ptrs) == ALIAS
+    # adjacent but disjoint ranges are fine up to the first launch: check with an
+    # empty problem so that nothing is launched
+    assert call_bob(lib, N=0, ptrs=[fb[m] for m in range(16)]) == OK
+
+
+def test_pass_entry_points_validate_too(lib):
+    fb = FakeBuffers(16)
+    p = [fb[m] for m in range(16)]
+    s = ctypes.c_void_p(0)
+    assert lib.fbob_bob_pass1(1, 1, 2, 2, 64, 80, ctypes.c_float(0.1), 0, *p[:14], s) == UNSUPPORTED
+    assert lib.fbob_bob_pass2(1, 1, 2, 2, 64, 80, ctypes.c_float(0.1), 0, *p[:13], s) == UNSUPPORTED
+    assert lib.fbob_bob_pass1(1, 1, 2, 2, 0, 64, ctypes.c_float(0.1), 0, *p[:14], s) == OK
+    q = list(p[:13])
+    q[12] = ctypes.c_void_p(fb.addrs[0])  # dVt aliases Q
+    assert lib.fbob_bob_pass2(1, 1, 2, 2, 64, 64, ctypes.c_float(0.1), 0, *q, s) == ALIAS
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load_library(str(tmp_path / "libfbob.so"))

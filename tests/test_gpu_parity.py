@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name before it touches the GPU.  Inputs are seeded
+(workloads.make_inputs); bf16 inputs are rounded to bf16 before either side
+sees them.  Bars: max|gpu - ref| / max|ref| per output tensor <= 1e-3 (fp32
+inputs) or <= 2e-2 (bf16 inputs).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import _gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def case(name, B, H, N, d, dtype, seed, causal=False, Hkv=None, **kw):
+    extra = {"Hkv": Hkv} if Hkv else {}
+    return workloads.Workload(name, B=B, H=H, N=N, d=d, dtype=dtype, seed=seed, causal=causal,
+                              extra=extra, **kw)
+
+
+SMALL = [
+    W["single_head_n128_d64_f32"],
+    case("n1_bf16", 1, 1, 1, 64, "bf16", 11),
+    case("n17_h2_bf16", 1, 2, 17, 64, "bf16", 12),
+    case("n300_b2_h3_bf16_ragged", 2, 3, 300, 64, "bf16", 13),
+    case("n129_d128_h2_bf16", 1, 2, 129, 128, "bf16", 14),
+    case("n200_d128_f32", 1, 1, 200, 128, "f32", 15),
+    case("n77_h2_f32_causal", 1, 2, 77, 64, "f32", 16, causal=True),
+    case("n333_h2_bf16_causal", 1, 2, 333, 64, "bf16", 17, causal=True),
+    case("n256_d128_h2_bf16_causal", 1, 2, 256, 128, "bf16", 18, causal=True),
+    case("gqa_hq4_hkv2_n200_bf16", 1, 4, 200, 64, "bf16", 19, Hkv=2),
+    case("gqa_hq6_hkv2_n160_bf16_causal", 1, 6, 160, 64, "bf16", 20, causal=True, Hkv=2),
+    case("mqa_hq3_hkv1_n96_d128_bf16", 1, 3, 96, 128, "bf16", 21, Hkv=1),
+    case("n1000_u01_qk2_bf16", 1, 1, 1000, 64, "bf16", 22, scale_u=0.1, scale_qk=2.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_cases_full_oracle(w):
+    U.say(f"[parity] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    inp = U.make_inputs(w)
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    ref = U.oracle_full(inp, w)
+    errs = U.compare_full(gpu, ref, w)
+    U.say(f"[parity] {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    tol = U.TOL[w.dtype]
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{w.name}: over {tol}: {bad}"
+
+
+def test_gpt2_heads_full_oracle():
+    w = W["gpt2_heads_h12_n4096_d64_bf16"]
+    U.say(f"[parity] {w.name}")
+    inp = U.make_inputs(w)
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    ref = U.oracle_full(inp, w)
+    errs = U.compare_full(gpu, ref, w)
+    U.say(f"[parity] {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+
+
+def test_headline_n16k_two_heads_full_and_sampled_rows():
+    """h12_n16384_d64 (U x 0.1): full oracle on heads 0 and 11, sampled rows on all."""
+    w = W["h12_n16384_d64_bf16_u01"]
+    U.say(f"[parity] {w.name}")
+    inp = U.make_inputs(w)
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    ref = U.oracle_full(inp, w, heads=[(0, 0), (0, 11)], blocked=True)
+    errs = U.compare_full(gpu, ref, w, keys=U.ALL_KEYS)
+    U.say(f"[parity] {w.name} heads 0,11: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+    _check_sampled_rows(w, inp, gpu, n_rows=16)
+    _check_invariants(gpu)
+
+
+def _check_sampled_rows(w, inp, gpu, n_rows):
+    rng = np.random.default_rng(7)
+    q, k = U.split_inputs(inp, w)
+    a = {key: [] for key in ("dQt", "ddOt", "alpha", "E", "O", "L", "D")}
+    r = {key: [] for key in a}
+    for (b, h) in U.head_list(w):
+        rows = np.sort(rng.choice(w.N, size=n_rows, replace=False))
+        rows[-1] = w.N - 1  # always include the ragged/last row
+        o = oracle.bob_rows(q("Q", b, h), k("K", b, h), k("V", b, h), q("dO", b, h),
+                            q("UQ", b, h), k("UK", b, h), k("UV", b, h), w.tau, rows, w.causal)
+        for key in a:
+            a[key].append(gpu[key][b, h][rows].ravel())
+            r[key].append(o[key].ravel())
+    errs = {key: U.rel(np.concatenate(a[key]), np.concatenate(r[key])) for key in a}
+    U.say(f"[parity] {w.name} sampled rows: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+
+
+def _check_invariants(gpu):
+    """Column sums of dK~ and dV~ vanish exactly (Phi is invariant under K -> K + 1c^T
+    and V -> V + 1c^T); with per-element rounding the sum over N keys is tiny
+    compared with the sum of magnitudes."""
+    for key in ("dKt", "dVt"):
+        x = gpu[key]
+        s = np.abs(x.sum(axis=2))
+        m = np.abs(x).sum(axis=2)
+        ratio = float(np.max(s / np.maximum(m, 1e-30)))
+        U.say(f"[parity] invariant sum_j {key}: max ratio {ratio:.2e}")
+        assert ratio < 1e-2, (key, ratio)
+
+
+@pytest.mark.parametrize("name", ["h8_n65536_d128_bf16_qk2", "h1_n262144_d64_bf16"])
+def test_large_sampled_rows_and_invariants(name):
+    w = W[name]
+    U.say(f"[parity] {w.name}")
+    inp = U.make_inputs(w)
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    _check_sampled_rows(w, inp, gpu, n_rows=8 if w.H > 1 else 32)
+    _check_invariants(gpu)
+
+
+def test_bitwise_deterministic():
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    w = case("det_n700_h3_bf16", 1, 3, 700, 64, "bf16", 31)
+    U.say(f"[parity] {w.name}")
+    dev = U.to_device(U.make_inputs(w), w.dtype)
+    O, L, D = fb.forward(dev["Q"], dev["K"], dev["V"], dev["dO"], w.tau)
+    args = (dev["Q"], dev["K"], dev["V"], dev["dO"], dev["UQ"], dev["UK"], dev["UV"], O, L, D)
+    a = fb.bob(*args, w.tau)
+    b = fb.bob(*args, w.tau)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_passes_separately_equal_fused_call():
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    w = case("split_n260_h2_bf16", 1, 2, 260, 64, "bf16", 32)
+    U.say(f"[parity] {w.name}")
+    dev = U.to_device(U.make_inputs(w), w.dtype)
+    O, L, D = fb.forward(dev["Q"], dev["K"], dev["V"], dev["dO"], w.tau)
+    args = (dev["Q"], dev["K"], dev["V"], dev["dO"], dev["UQ"], dev["UK"], dev["UV"])
+    full = fb.bob(*args, O, L, D, w.tau)
+    p1 = fb.bob_pass1(*args, O, L, D, w.tau)
+    p2 = fb.bob_pass2(*args, L, D, p1["alpha"], p1["E"], w.tau)
+    torch.cuda.synchronize()
+    for k in p1:
+        assert torch.equal(p1[k], full[k]), k
+    for k in p2:
+        assert torch.equal(p2[k], full[k]), k
+
+
+def test_empty_problem_writes_nothing():
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    U.say("[parity] empty N=0")
+    z = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    O, L, D = fb.forward(z, z, z, z)
+    out = fb.bob(z, z, z, z, z, z, z, O, L, D)
+    torch.cuda.synchronize()
+    assert all(v.numel() == 0 for v in out.values())
