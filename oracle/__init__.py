@@ -27,6 +27,7 @@ from .fbob_oracle import (  # noqa: F401
     bob,
     bob_affine,
     bob_rows,
+    bob_row_block,
     bob_blocked,
     bob_columns,
 )

@@ -214,6 +214,20 @@ def bob_rows(Q, K, V, dO, UQ, UK, UV, tau, rows, causal=False):
                 L=r["L"], D=r["D"], O=r["O"])
 
 
+def bob_row_block(Q, K, V, dO, UQ, UK, UV, tau, rows, causal=False):
+    """One block of full-width rows: its row outputs and its share of dK~, dV~.
+
+    dK~ and dV~ are sums over rows; summing the returned dKt_part/dVt_part over a
+    partition of the rows gives the full column outputs.
+    """
+    rows = np.asarray(rows)
+    Q, K, V, dO, UQ, UK, UV = map(_f64, (Q, K, V, dO, UQ, UK, UV))
+    r = _row_chain(Q[rows], dO[rows], UQ[rows], K, V, UK, UV, tau, causal, rows)
+    return dict(dQt=r["dQt"], ddOt=r["ddOt"], alpha=r["alpha"], E=r["E"],
+                dKt_part=tau * (r["dSt"].T @ Q[rows] + r["dS"].T @ UQ[rows]),
+                dVt_part=r["ddP"].T @ dO[rows])
+
+
 def bob_blocked(Q, K, V, dO, UQ, UK, UV, tau, causal=False, row_block=1024):
     """All BoB outputs for one head, rows taken ``row_block`` at a time.
 
@@ -227,13 +241,11 @@ def bob_blocked(Q, K, V, dO, UQ, UK, UV, tau, causal=False, row_block=1024):
                alpha=np.empty(N), E=np.empty(N))
     for r0 in range(0, N, row_block):
         rows = np.arange(r0, min(N, r0 + row_block))
-        r = _row_chain(Q[rows], dO[rows], UQ[rows], K, V, UK, UV, tau, causal, rows)
-        out["dQt"][rows] = r["dQt"]
-        out["ddOt"][rows] = r["ddOt"]
-        out["alpha"][rows] = r["alpha"]
-        out["E"][rows] = r["E"]
-        out["dKt"] += tau * (r["dSt"].T @ Q[rows] + r["dS"].T @ UQ[rows])
-        out["dVt"] += r["ddP"].T @ dO[rows]
+        r = bob_row_block(Q, K, V, dO, UQ, UK, UV, tau, rows, causal)
+        for k in ("dQt", "ddOt", "alpha", "E"):
+            out[k][rows] = r[k]
+        out["dKt"] += r["dKt_part"]
+        out["dVt"] += r["dVt_part"]
     return out
 
 
