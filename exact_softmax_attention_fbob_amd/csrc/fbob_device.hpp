@@ -26,6 +26,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Keeps the machine scheduler from hoisting loads across phases of a tile (it
+// otherwise front-loads every LDS fragment and runs out of registers).
+#ifndef FBOB_NO_SCHED_FENCE
+#define FBOB_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define FBOB_SCHED_FENCE() ((void)0)
+#endif
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
@@ -161,7 +169,12 @@ __device__ __forceinline__ typename Elem<T>::frag global_frag(const T* base, int
   using F = typename Elem<T>::frag;
   F o;
   if (row < nrows) {
-    o = *reinterpret_cast<const F*>(base + (int64_t)row * ld + col);
+    if constexpr (sizeof(T) == 2) {
+      o = *reinterpret_cast<const F*>(base + (int64_t)row * ld + col);
+    } else {
+      const f32x4* p = reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + col);
+      o = Elem<T>::from_f32(p[0], p[1]);
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (T)0.0f;
@@ -171,14 +184,15 @@ __device__ __forceinline__ typename Elem<T>::frag global_frag(const T* base, int
 
 // ---------------------------------------------------------------------------
 // Tile staging: global (rows row0.., D columns, contiguous) -> registers -> LDS.
-// Rows at or past `nrows` are zero-filled.  kPer = 16-byte chunks per thread.
+// Rows at or past `nrows` are zero-filled.  kPer = 16-byte chunks per thread
+// (the last round may leave threads idle when the count does not divide).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int ROWS, int NTHREADS>
 struct Stager {
   static constexpr int kChunks = Tile<T, D>::kChunks;
   static constexpr int kTotal = ROWS * kChunks;
-  static_assert(kTotal % NTHREADS == 0, "tile chunks must divide evenly over threads");
-  static constexpr int kPer = kTotal / NTHREADS;
+  static constexpr int kPer = (kTotal + NTHREADS - 1) / NTHREADS;
+  static constexpr bool kEven = kTotal % NTHREADS == 0;
   u32x4 v[kPer];
 
   __device__ __forceinline__ void load(const T* src, int row0, int nrows, int tid) {
@@ -187,7 +201,7 @@ struct Stager {
     for (int k = 0; k < kPer; ++k) {
       const int idx = tid + k * NTHREADS;
       const int row = idx / kChunks, c = idx % kChunks;
-      if (row0 + row < nrows) {
+      if ((kEven || idx < kTotal) && row0 + row < nrows) {
         v[k] = *reinterpret_cast<const u32x4*>(s + (int64_t)(row0 + row) * Tile<T, D>::kRowBytes + c * 16);
       } else {
         v[k] = u32x4{0u, 0u, 0u, 0u};
@@ -199,10 +213,150 @@ struct Stager {
     for (int k = 0; k < kPer; ++k) {
       const int idx = tid + k * NTHREADS;
       const int row = idx / kChunks, c = idx % kChunks;
-      *reinterpret_cast<u32x4*>(tile + Tile<T, D>::chunk_off(row, c)) = v[k];
+      if (kEven || idx < kTotal)
+        *reinterpret_cast<u32x4*>(tile + Tile<T, D>::chunk_off(row, c)) = v[k];
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// Staging of NT same-shaped tiles (ROWS rows each) in one pass: the NT * ROWS *
+// chunks 16-byte chunks are spread evenly over the work-group.  Rows past the
+// end are clamped to the last row (finite data; every consumer gives them zero
+// weight), so the loads need no predication.  The tiles are stored back to back
+// in LDS, kTileBytes apart.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int ROWS, int NT, int NTHREADS>
+struct MultiStager {
+  static constexpr int kRB = Tile<T, D>::kRowBytes;
+  static constexpr int kChunks = Tile<T, D>::kChunks;
+  static constexpr int kPerTensor = ROWS * kChunks;
+  static constexpr int kTotal = NT * kPerTensor;
+  static_assert(kTotal % NTHREADS == 0, "staged chunks must divide evenly over threads");
+  static constexpr int kPer = kTotal / NTHREADS;
+  static constexpr int kTileBytes = ROWS * kRB;
+  const char* src[kPer];  // tensor base + chunk column, per owned chunk
+  int row[kPer];          // row within the tile
+  int lds_off[kPer];      // tensor tile offset + swizzled chunk offset
+  u32x4 v[kPer];
+
+  // `bases` are the NT tensor bases (element pointers of the current head).
+  __device__ __forceinline__ void init(const T* const (&bases)[NT], int tid) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = tid + k * NTHREADS;
+      const int tensor = idx / kPerTensor, rem = idx % kPerTensor;
+      row[k] = rem / kChunks;
+      const int c = rem % kChunks;
+      const T* base = bases[0];
+#pragma unroll
+      for (int m = 1; m < NT; ++m)
+        if (tensor == m) base = bases[m];
+      src[k] = reinterpret_cast<const char*>(base) + c * 16;
+      lds_off[k] = tensor * kTileBytes + Tile<T, D>::chunk_off(row[k], c);
+    }
+  }
+  // Retarget the chunks to new tensor bases (same layout), e.g. another head.
+  __device__ __forceinline__ void rebase(const T* const (&bases)[NT], int tid) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = tid + k * NTHREADS;
+      const int tensor = idx / kPerTensor, c = (idx % kPerTensor) % kChunks;
+      const T* base = bases[0];
+#pragma unroll
+      for (int m = 1; m < NT; ++m)
+        if (tensor == m) base = bases[m];
+      src[k] = reinterpret_cast<const char*>(base) + c * 16;
+    }
+  }
+  // `byte_off` shifts every tensor by the same amount (another head of the same
+  // shape); rows are clamped to nrows - 1.
+  __device__ __forceinline__ void load(int row0, int nrows, int64_t byte_off = 0) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int gr = min(row0 + row[k], nrows - 1);
+      v[k] = *reinterpret_cast<const u32x4*>(src[k] + byte_off + (int64_t)gr * kRB);
+    }
+  }
+  __device__ __forceinline__ void store(char* tiles) const {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) *reinterpret_cast<u32x4*>(tiles + lds_off[k]) = v[k];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Per-lane LDS fragment reader for 32-row staged tiles.  The swizzled byte
+// offsets that depend only on the lane are computed once; a read is then a
+// tile base plus a compile-time constant plus one of these registers.
+//   row(tile, rb, dc): A/B operand rows 16 rb + r, columns 32 dc + 8 g .. +7
+//   tr(tile, db):      transposed operand, lane (r, g) gets X[k(g, e)][16 db + r]
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct LdsLane {
+  static constexpr int kRB = Tile<T, D>::kRowBytes;
+  static constexpr int kDC = D / 32, kDB = D / 16;
+  int ro[kDC];
+  int to[kDB];
+  int r, g;
+
+  __device__ __forceinline__ LdsLane(int r_, int g_) : r(r_), g(g_) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int dc = 0; dc < kDC; ++dc) ro[dc] = Tile<T, D>::chunk_off(r, 4 * dc + g);
+      const int b = r >> 2, c = r & 3;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) to[db] = Tile<T, D>::elem_off(4 * g + b, 16 * db + 4 * c);
+    }
+  }
+  __device__ __forceinline__ typename Elem<T>::frag row(const char* tile, int rb, int dc) const {
+    using F = typename Elem<T>::frag;
+    if constexpr (sizeof(T) == 2) {
+      return *reinterpret_cast<const F*>(tile + rb * 16 * kRB + ro[dc]);
+    } else {
+      return lds_frag_row<T, D>(tile, 16 * rb + r, 32 * dc + 8 * g);
+    }
+  }
+  __device__ __forceinline__ typename Elem<T>::frag tr(const char* tile, int db) const {
+    if constexpr (sizeof(T) == 2) {
+#if FBOB_NO_TR_READ
+      return lds_frag_tr<T, D>(tile, 0, 16 * db, r, g);
+#else
+      typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+      const uintptr_t base = reinterpret_cast<uintptr_t>(tile) + to[db];
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 16 * kRB));
+      typename Elem<T>::frag o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o[q] = lo[q];
+        o[4 + q] = hi[q];
+      }
+      return o;
+#endif
+    } else {
+      return lds_frag_tr<T, D>(tile, 0, 16 * db, r, g);
+    }
+  }
+};
+
+// Operand fragment scaled by s (fp32 product, rounded back to T).  Exact for
+// bf16 when s is a power of two.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag scale_frag(typename Elem<T>::frag f, float s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (T)((float)f[e] * s);
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag ones_frag() {
+  typename Elem<T>::frag f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (T)1.0f;
+  return f;
+}
+
+__device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
 
 // Sum over the four 16-lane groups (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float group_sum(float x) {

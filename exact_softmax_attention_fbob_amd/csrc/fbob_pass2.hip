@@ -12,36 +12,42 @@
 // summing all query heads of a key/value group on chip, then writes dK~ and dV~
 // exactly once, with no atomics.
 //
-// Schedule: one work-group = 4 waves; each wave owns 16*NJ key positions whose
-// K, V, U_K, U_V operand fragments and the two fp32 accumulators stay in
-// registers.  Q, dO, U_Q row tiles of 32 rows plus their four row scalars are
-// staged through LDS (double-buffered).  Scores are computed with the query index
-// on the MFMA row axis, so a lane owns one key and four consecutive rows per
-// block; those C registers are directly the B operand of the contractions over
-// rows, whose A operand (Q^T, U_Q^T, dO^T) comes from transposed LDS reads.
+// With t = dP - D, u = F - alpha and g' = G - E - alpha D, the adjoints are
+//   dS = P t,   ddP = P u,   dS~ = P (u t + g'),
+// and t, u, g' come straight out of the MFMAs by seeding their accumulators with
+// the row scalars -D, -alpha and -(E + alpha D); tau is folded into the resident
+// K and U_K operands of the F tile.  That leaves five VALU operations plus one exp
+// per score element.
+//
+// Schedule: one work-group = NW waves; each wave owns 16 key positions whose K,
+// tau K, tau U_K, V, U_V operand fragments and the two fp32 accumulators stay in
+// registers.  Q, dO, U_Q row tiles (kBRs rows) plus the four derived row scalars
+// are staged through LDS (double-buffered).  Scores are computed with the query
+// index on the MFMA row axis, so a lane owns one key and four consecutive rows
+// per block; those C registers are directly the B operand of the contractions
+// over rows, whose A operand (Q^T, U_Q^T, dO^T) comes from transposed LDS reads.
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
 namespace fbob {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBRs = 32;  // rows per LDS stage
-
-template <typename T, int D, int NJ, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
-                                                         float tau, int n_col_tiles, int total) {
+template <typename T, int D, int NW, int BRS, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
+                                                        float tau, int n_col_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int kColsW = 16 * NJ;
-  constexpr int kBCw = 4 * kColsW;
-  constexpr int kTB = kBRs * Tile<T, D>::kRowBytes;
+  constexpr int kThreads = NW * 64;
+  constexpr int kBCw = NW * 16;                     // keys per work-group
+  constexpr int kTB = BRS * Tile<T, D>::kRowBytes;  // bytes per staged tile
   constexpr int kDC = D / 32;
   constexpr int kDB = D / 16;
-  constexpr int kScal = 4 * kBRs * 4;  // L, D, alpha, E for the stage rows (bytes)
-  __shared__ __attribute__((aligned(16))) char lds[2][3 * kTB + kScal];
+  constexpr int kScal = 4 * BRS * 4;                // -L log2e, -D, -alpha, -(E + alpha D)
+  constexpr int kStage = 3 * kTB + kScal;
+  __shared__ __attribute__((aligned(16))) char lds[2][kStage];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
   const int bhk = logical / n_col_tiles, ct = logical % n_col_tiles;
@@ -53,183 +59,172 @@ __global__ __launch_bounds__(kThreads) void pass2_kernel(Pass2Args a, int Hkv, i
   const T* UKh = reinterpret_cast<const T*>(a.UK) + kv_off;
   const T* UVh = reinterpret_cast<const T*>(a.UV) + kv_off;
 
-  const int jw0 = ct * kBCw + w * kColsW;
-  F kf[NJ][kDC], vf[NJ][kDC], ukf[NJ][kDC], uvf[NJ][kDC];
+  const int jw0 = ct * kBCw + w * 16;
+  const int j = jw0 + r;  // this lane's key
+  F kf[kDC], tkf[kDC], tukf[kDC], vf[kDC], uvf[kDC];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
-#pragma unroll
-    for (int dc = 0; dc < kDC; ++dc) {
-      const int j = jw0 + 16 * jb + r, col = 32 * dc + 8 * g;
-      kf[jb][dc] = global_frag(Kh, j, N, D, col);
-      vf[jb][dc] = global_frag(Vh, j, N, D, col);
-      ukf[jb][dc] = global_frag(UKh, j, N, D, col);
-      uvf[jb][dc] = global_frag(UVh, j, N, D, col);
-    }
+  for (int dc = 0; dc < kDC; ++dc) {
+    const int col = 32 * dc + 8 * g;
+    kf[dc] = global_frag(Kh, j, N, D, col);
+    tkf[dc] = scale_frag<T>(kf[dc], tau);
+    tukf[dc] = scale_frag<T>(global_frag(UKh, j, N, D, col), tau);
+    vf[dc] = global_frag(Vh, j, N, D, col);
+    uvf[dc] = global_frag(UVh, j, N, D, col);
+  }
 
-  f32x4 accK[NJ][kDB], accV[NJ][kDB];
+  f32x4 accK[kDB], accV[kDB];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      accK[jb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accV[jb][db] = accK[jb][db];
-    }
+  for (int db = 0; db < kDB; ++db) {
+    accK[db] = splat4(0.f);
+    accV[db] = accK[db];
+  }
   const float c1 = tau * kLog2e;
+  const LdsLane<T, D> rd(r, g);
 
-  // Row chunks: causal rows start at the work-group's first key.
-  const int i_begin = CAUSAL ? (ct * kBCw / kBRs) * kBRs : 0;
-  const int nrc = (N - i_begin + kBRs - 1) / kBRs;
-  const int nsteps = nrc * group;  // (query head of the group, row chunk)
+  // Row steps: (query head of the group, row chunk); causal rows start at the
+  // work-group's first key.
+  const int i_begin = CAUSAL ? (ct * kBCw / BRS) * BRS : 0;
+  const int nrc = (N - i_begin + BRS - 1) / BRS;
+  const int nsteps = nrc * group;
 
-  Stager<T, D, kBRs, kThreads> sq, sdo, suq;
-  const T* const Qg = reinterpret_cast<const T*>(a.Q);
-  const T* const dOg = reinterpret_cast<const T*>(a.dO);
-  const T* const UQg = reinterpret_cast<const T*>(a.UQ);
-  // Row scalar streamed by this thread (tid < 4 * kBRs): L, D, alpha or E.
-  const int which = tid / kBRs;
-  const float* const scal_src = which == 0 ? a.L : which == 1 ? a.D : which == 2 ? a.alpha : a.E;
-  float sc_v = 0.f;
+  const int64_t q_head = (int64_t)N * D * (int64_t)sizeof(T);  // bytes per query head
+  const int64_t q0 = ((int64_t)b * Hq + (int64_t)hk * group) * N * D;
+  const T* const q_bases[3] = {reinterpret_cast<const T*>(a.Q) + q0,
+                               reinterpret_cast<const T*>(a.dO) + q0,
+                               reinterpret_cast<const T*>(a.UQ) + q0};
+  MultiStager<T, D, BRS, 3, kThreads> st;
+  st.init(q_bases, tid);
+  // Row scalars: thread tid < BRS stages row tid of the chunk.
+  const int64_t s0 = ((int64_t)b * Hq + (int64_t)hk * group) * N;
+  f32x4 scal = splat4(0.f);
   auto load_step = [&](int step) {
-    const int hq = hk * group + step / nrc;
-    const int i0 = i_begin + (step % nrc) * kBRs;
-    const int64_t q_off = ((int64_t)b * Hq + hq) * N * D;
-    sq.load(Qg + q_off, i0, N, tid);
-    sdo.load(dOg + q_off, i0, N, tid);
-    suq.load(UQg + q_off, i0, N, tid);
-    if (tid < 4 * kBRs) {
-      const int i = i0 + tid % kBRs;
-      sc_v = i < N ? scal_src[((int64_t)b * Hq + hq) * N + i] : 0.f;
+    const int hq = step / nrc;
+    const int i0 = i_begin + (step % nrc) * BRS;
+    st.load(i0, N, hq * q_head);
+    if (tid < BRS) {
+      const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
+      const float L = a.L[ri], Dv = a.D[ri], al = a.alpha[ri], Ev = a.E[ri];
+      scal = f32x4{-L * kLog2e, -Dv, -al, -(Ev + al * Dv)};
     }
   };
   auto store_step = [&](char* buf) {
-    sq.store(buf, tid);
-    sdo.store(buf + kTB, tid);
-    suq.store(buf + 2 * kTB, tid);
-    if (tid < 4 * kBRs) reinterpret_cast<float*>(buf + 3 * kTB)[tid] = sc_v;
+    st.store(buf);
+    if (tid < BRS) {
+      float* sp = reinterpret_cast<float*>(buf + 3 * kTB);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sp[m * BRS + tid] = scal[m];
+    }
+  };
+
+  // 32 rows of a staged tile (sub-chunk sc): scores, elementwise, contractions.
+  auto chunk = [&](const char* buf, int i0, int sc) {
+    const char* Qt = buf;
+    const char* dOt = buf + kTB;
+    const char* UQt = buf + 2 * kTB;
+    const float* sp = reinterpret_cast<const float*>(buf + 3 * kTB);
+    const int ic = i0 + 32 * sc;
+    const bool edge = (ic + 32 > N) || (CAUSAL && ic < jw0 + 15);
+    f32x4 vds[2], vddp[2], vdst[2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int rr = 32 * sc + 16 * ib + 4 * g;  // first of this lane's 4 rows in the tile
+      const f32x4 nL = *reinterpret_cast<const f32x4*>(sp + rr);
+      f32x4 s = splat4(0.f);
+      f32x4 t = *reinterpret_cast<const f32x4*>(sp + BRS + rr);
+      f32x4 u = *reinterpret_cast<const f32x4*>(sp + 2 * BRS + rr);
+      f32x4 gp = *reinterpret_cast<const f32x4*>(sp + 3 * BRS + rr);
+#pragma unroll
+      for (int dc = 0; dc < kDC; ++dc) {
+        const F qa = rd.row(Qt, 2 * sc + ib, dc);
+        const F doa = rd.row(dOt, 2 * sc + ib, dc);
+        const F uqa = rd.row(UQt, 2 * sc + ib, dc);
+        s = E::mma(qa, kf[dc], s);
+        u = E::mma(uqa, tkf[dc], u);
+        u = E::mma(qa, tukf[dc], u);
+        t = E::mma(doa, vf[dc], t);
+        gp = E::mma(doa, uvf[dc], gp);
+      }
+      f32x4 p;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[q], c1, nL[q]));
+      if (edge) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = ic + 16 * ib + 4 * g + q;
+          if (i >= N || (CAUSAL && j > i)) p[q] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        vds[ib][q] = p[q] * t[q];
+        vddp[ib][q] = p[q] * u[q];
+        vdst[ib][q] = p[q] * __builtin_fmaf(u[q], t[q], gp[q]);
+      }
+    }
+    FBOB_SCHED_FENCE();
+    const F dsB = E::from_f32(vds[0], vds[1]);
+    const F ddpB = E::from_f32(vddp[0], vddp[1]);
+    const F dstB = E::from_f32(vdst[0], vdst[1]);
+    const char* Qs = Qt + 32 * sc * Tile<T, D>::kRowBytes;
+    const char* dOs = dOt + 32 * sc * Tile<T, D>::kRowBytes;
+    const char* UQs = UQt + 32 * sc * Tile<T, D>::kRowBytes;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      FBOB_SCHED_FENCE();
+      const F qt = rd.tr(Qs, db);
+      const F uqt = rd.tr(UQs, db);
+      const F dot = rd.tr(dOs, db);
+      accK[db] = E::mma(qt, dstB, accK[db]);
+      accK[db] = E::mma(uqt, dsB, accK[db]);
+      accV[db] = E::mma(dot, ddpB, accV[db]);
+    }
   };
 
   load_step(0);
   store_step(lds[0]);
   __syncthreads();
 
-  for (int t = 0; t < nsteps; ++t) {
-    const int i0 = i_begin + (t % nrc) * kBRs;
+  auto step = [&](int t, char* cur, char* nxt) {
+    const int i0 = i_begin + (t % nrc) * BRS;
     const bool more = t + 1 < nsteps;
     if (more) load_step(t + 1);
-    const char* Qt = lds[t & 1];
-    const char* dOt = Qt + kTB;
-    const char* UQt = Qt + 2 * kTB;
-    const float* sc = reinterpret_cast<const float*>(Qt + 3 * kTB);
-    const bool active = !CAUSAL || i0 + kBRs - 1 >= jw0;
-    if (active) {
-      // ---- score-shaped tiles: [row block ib][key block jb] ----
-      f32x4 s[2][NJ], dp[2][NJ], f[2][NJ], gg[2][NJ];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) {
-          s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[ib][jb] = s[ib][jb];
-          f[ib][jb] = s[ib][jb];
-          gg[ib][jb] = s[ib][jb];
-        }
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int dc = 0; dc < kDC; ++dc) {
-          const int row = 16 * ib + r, col = 32 * dc + 8 * g;
-          const F qa = lds_frag_row<T, D>(Qt, row, col);
-          const F doa = lds_frag_row<T, D>(dOt, row, col);
-          const F uqa = lds_frag_row<T, D>(UQt, row, col);
-#pragma unroll
-          for (int jb = 0; jb < NJ; ++jb) {
-            s[ib][jb] = E::mma(qa, kf[jb][dc], s[ib][jb]);
-            f[ib][jb] = E::mma(uqa, kf[jb][dc], f[ib][jb]);
-            f[ib][jb] = E::mma(qa, ukf[jb][dc], f[ib][jb]);
-            dp[ib][jb] = E::mma(doa, vf[jb][dc], dp[ib][jb]);
-            gg[ib][jb] = E::mma(doa, uvf[jb][dc], gg[ib][jb]);
-          }
-        }
-      // ---- elementwise with per-row scalars (rows 16 ib + 4 g + q) ----
-      const bool edge = (i0 + kBRs > N) || (CAUSAL && i0 < jw0 + kColsW - 1);
-      F dstB[NJ], dsB[NJ], ddpB[NJ];
-      f32x4 vdst[NJ][2], vds[NJ][2], vddp[NJ][2];
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        const int rr = 16 * ib + 4 * g;
-        const f32x4 Lr = *reinterpret_cast<const f32x4*>(sc + rr) * kLog2e;
-        const f32x4 Dr = *reinterpret_cast<const f32x4*>(sc + kBRs + rr);
-        const f32x4 Ar = *reinterpret_cast<const f32x4*>(sc + 2 * kBRs + rr);
-        const f32x4 Er = *reinterpret_cast<const f32x4*>(sc + 3 * kBRs + rr);
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float p = fast_exp2(s[ib][jb][q] * c1 - Lr[q]);
-            if (edge) {
-              const int i = i0 + rr + q, j = jw0 + 16 * jb + r;
-              if (i >= N || (CAUSAL && j > i)) p = 0.f;
-            }
-            const float dpv = dp[ib][jb][q];
-            const float tv = dpv - Dr[q];
-            const float fv = f[ib][jb][q] * tau;
-            const float dpt = fv * tv - Ar[q] * dpv + gg[ib][jb][q];
-            vds[jb][ib][q] = p * tv;
-            vdst[jb][ib][q] = p * (dpt - Er[q]);
-            vddp[jb][ib][q] = p * (fv - Ar[q]);
-          }
-      }
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        dstB[jb] = E::from_f32(vdst[jb][0], vdst[jb][1]);
-        dsB[jb] = E::from_f32(vds[jb][0], vds[jb][1]);
-        ddpB[jb] = E::from_f32(vddp[jb][0], vddp[jb][1]);
-      }
-      // ---- contractions over the stage's 32 rows (transposed outputs) ----
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const F qt = lds_frag_tr<T, D>(Qt, 0, 16 * db, r, g);
-        const F uqt = lds_frag_tr<T, D>(UQt, 0, 16 * db, r, g);
-        const F dot = lds_frag_tr<T, D>(dOt, 0, 16 * db, r, g);
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) {
-          accK[jb][db] = E::mma(qt, dstB[jb], accK[jb][db]);
-          accK[jb][db] = E::mma(uqt, dsB[jb], accK[jb][db]);
-          accV[jb][db] = E::mma(dot, ddpB[jb], accV[jb][db]);
-        }
-      }
+    for (int sc = 0; sc < BRS / 32; ++sc) {
+      const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
+      if (active) chunk(cur, i0, sc);
     }
-    if (more) store_step(lds[(t + 1) & 1]);
+    if (more) store_step(nxt);
     __syncthreads();
+  };
+#pragma unroll 1
+  for (int t = 0; t < nsteps; t += 2) {
+    step(t, lds[0], lds[1]);
+    if (t + 1 < nsteps) step(t + 1, lds[1], lds[0]);
   }
 
   // ---- single exclusive write of dK~ and dV~ ----
+  if (j < N) {
+    const int64_t ro = kv_off + (int64_t)j * D;
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) {
-    const int j = jw0 + 16 * jb + r;
-    if (j < N) {
-      const int64_t ro = kv_off + (int64_t)j * D;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const int d0 = 16 * db + 4 * g;
-        *reinterpret_cast<f32x4*>(a.dKt + ro + d0) = tau * accK[jb][db];
-        *reinterpret_cast<f32x4*>(a.dVt + ro + d0) = accV[jb][db];
-      }
+    for (int db = 0; db < kDB; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      *reinterpret_cast<f32x4*>(a.dKt + ro + d0) = tau * accK[db];
+      *reinterpret_cast<f32x4*>(a.dVt + ro + d0) = accV[db];
     }
   }
 }
 
-template <typename T, int D, int NJ>
+template <typename T, int D, int NW, int BRS>
 hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
-  constexpr int kBCw = 4 * 16 * NJ;
+  constexpr int kBCw = NW * 16;
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
   const int total = n_col_tiles * p.B * p.Hkv;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass2_kernel<T, D, NJ, true>), dim3(total), dim3(kThreads), 0, s, a, p.Hkv,
-                       group, p.N, p.tau, n_col_tiles, total);
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, BRS, true>), dim3(total), dim3(NW * 64), 0, s, a,
+                       p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   else
-    hipLaunchKernelGGL((pass2_kernel<T, D, NJ, false>), dim3(total), dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, BRS, false>), dim3(total), dim3(NW * 64), 0, s, a,
                        p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   return hipGetLastError();
 }
@@ -238,11 +233,11 @@ hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
 
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
   if (p.bf16) {
-    if (p.d == 64) return launch_t<__bf16, 64, 2>(p, a, s);
-    return launch_t<__bf16, 128, 1>(p, a, s);
+    if (p.d == 64) return launch_t<__bf16, 64, 8, 64>(p, a, s);
+    return launch_t<__bf16, 128, 4, 32>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 1>(p, a, s);
-  return launch_t<float, 128, 1>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 32>(p, a, s);
+  return launch_t<float, 128, 4, 32>(p, a, s);
 }
 
 }  // namespace fbob
