@@ -80,16 +80,29 @@ template <> struct Elem<float> {
 
 // ---------------------------------------------------------------------------
 // LDS tile: R rows x D columns of T, row-major, 16-byte chunks XOR-swizzled
-// within a row so that (a) eight consecutive rows read at one column chunk and
-// (b) the 4-row x 32-byte pattern of a transposed read both hit distinct banks.
+// within a row so that the three access patterns of the kernels are free of
+// bank conflicts on gfx950:
+//   (a) b128 fragment reads: 16 consecutive rows at one logical chunk;
+//   (b) transposed b64 reads: 4 rows x 32 bytes per 16-lane group;
+//   (c) b128 staging writes of consecutive chunks.
+// 128-byte rows (bf16, d = 64): the XOR mask is an invertible map of row bits
+// 1..3, (r2) | (r2 ^ r3) << 1 | (r1) << 2, chosen by measuring
+// SQ_LDS_BANK_CONFLICT for all 168 such maps on the three patterns (zero on
+// each); 256-byte and longer rows use a 16-valued mask of row bits 0..3, also
+// measured conflict-free on the three patterns.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
 template <typename T, int D>
 struct Tile {
   static constexpr int kRowBytes = D * (int)sizeof(T);
   static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row
   static_assert(kChunks >= 8, "swizzle needs at least 8 chunks per row");
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (kRowBytes == 128)
+      return ((row >> 2) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1) | (((row >> 1) & 1) << 2);
+    else
+      return ((row >> 1) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1) |
+             ((((row >> 1) ^ (row >> 2)) & 1) << 2) | ((row & 1) << 3);
+  }
   // byte offset of chunk c of row `row`
   static __device__ __forceinline__ int chunk_off(int row, int c) {
     return row * kRowBytes + ((c ^ swz(row)) << 4);

@@ -26,6 +26,8 @@
 // -D, giving dP - D directly), tau is folded into the resident operands of the F
 // tile, and the row sums alpha and E' are MFMA contractions with a ones operand,
 // which leaves seven VALU operations plus one exp per score element.
+#include <stdlib.h>
+
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
@@ -34,13 +36,14 @@ namespace {
 
 constexpr int kBC = 32;  // keys per LDS stage
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, int NI, bool FENCE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int kThreads = NW * 64;
-  constexpr int kBR = NW * 16;                       // query rows per work-group
+  constexpr int kRW = 16 * NI;                       // query rows per wave
+  constexpr int kBR = NW * kRW;                      // query rows per work-group
   constexpr int kTB = kBC * Tile<T, D>::kRowBytes;   // bytes per staged tile
   constexpr int kDC = D / 32;
   constexpr int kDB = D / 16;
@@ -63,29 +66,38 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
                                 reinterpret_cast<const T*>(a.UV) + kv_off};
 
   // ---- resident row operands (B operand of the transposed score tiles) ----
-  const int iw0 = rt * kBR + w * 16;
-  const int i = iw0 + r;  // this lane's query row
-  F qf[kDC], tqf[kDC], tuqf[kDC], dof[kDC];
+  const int iw0 = rt * kBR + w * kRW;
+  F qf[NI][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
+  float nl2[NI], dv[NI];
 #pragma unroll
-  for (int dc = 0; dc < kDC; ++dc) {
-    qf[dc] = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
-    tqf[dc] = scale_frag<T>(qf[dc], tau);
-    tuqf[dc] = scale_frag<T>(global_frag(UQh, i, N, D, 32 * dc + 8 * g), tau);
-    dof[dc] = global_frag(dOh, i, N, D, 32 * dc + 8 * g);
+  for (int ib = 0; ib < NI; ++ib) {
+    const int i = iw0 + 16 * ib + r;
+#pragma unroll
+    for (int dc = 0; dc < kDC; ++dc) {
+      qf[ib][dc] = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
+      tqf[ib][dc] = scale_frag<T>(qf[ib][dc], tau);
+      tuqf[ib][dc] = scale_frag<T>(global_frag(UQh, i, N, D, 32 * dc + 8 * g), tau);
+      dof[ib][dc] = global_frag(dOh, i, N, D, 32 * dc + 8 * g);
+    }
+    nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
+    dv[ib] = i < N ? a.D[(int64_t)bh * N + i] : 0.f;
   }
-  const float nl2 = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
-  const float dv = i < N ? a.D[(int64_t)bh * N + i] : 0.f;
   const F ones = ones_frag<T>();
 
-  f32x4 accB[kDB], accX[kDB], accW[kDB], accO[kDB];
+  f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
+  f32x4 accA[NI], accE[NI];  // alpha, E' (every q holds the row sum)
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) {
-    accB[db] = splat4(0.f);
-    accX[db] = accB[db];
-    accW[db] = accB[db];
-    accO[db] = accB[db];
+  for (int ib = 0; ib < NI; ++ib) {
+    accA[ib] = splat4(0.f);
+    accE[ib] = splat4(0.f);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      accB[ib][db] = splat4(0.f);
+      accX[ib][db] = accB[ib][db];
+      accW[ib][db] = accB[ib][db];
+      accO[ib][db] = accB[ib][db];
+    }
   }
-  f32x4 accA = splat4(0.f), accE = splat4(0.f);  // alpha, E' (every q holds the row sum)
   const float c1 = tau * kLog2e;
   const LdsLane<T, D> rd(r, g);
 
@@ -100,61 +112,83 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     const char* UKt = Kt + 2 * kTB;
     const char* UVt = Kt + 3 * kTB;
     const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > iw0);
-    // Scores and elementwise work one 16-key block at a time.
-    f32x4 vp[2], vds[2], vpf[2], vpw[2];
+    // Scores and elementwise work one 16-key block at a time; the K, V, U_K, U_V
+    // fragments of a block serve every row block of the wave.
+    f32x4 vp[NI][2], vds[NI][2], vpf[NI][2], vpw[NI][2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
-      f32x4 s = splat4(0.f), t = splat4(-dv), f = splat4(0.f), gg = splat4(0.f);
+      f32x4 s[NI], t[NI], f[NI], gg[NI];
+#pragma unroll
+      for (int ib = 0; ib < NI; ++ib) {
+        s[ib] = splat4(0.f);
+        t[ib] = splat4(-dv[ib]);
+        f[ib] = splat4(0.f);
+        gg[ib] = splat4(0.f);
+      }
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
         const F kf = rd.row(Kt, jb, dc);
         const F vf = rd.row(Vt, jb, dc);
         const F ukf = rd.row(UKt, jb, dc);
         const F uvf = rd.row(UVt, jb, dc);
-        s = E::mma(kf, qf[dc], s);
-        f = E::mma(kf, tuqf[dc], f);
-        f = E::mma(ukf, tqf[dc], f);
-        t = E::mma(vf, dof[dc], t);
-        gg = E::mma(uvf, dof[dc], gg);
-      }
-      f32x4 p;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[q], c1, nl2));
-      if (edge) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + 16 * jb + 4 * g + q;
-          if (j >= N || (CAUSAL && j > i)) p[q] = 0.f;
+        for (int ib = 0; ib < NI; ++ib) {
+          s[ib] = E::mma(kf, qf[ib][dc], s[ib]);
+          f[ib] = E::mma(kf, tuqf[ib][dc], f[ib]);
+          f[ib] = E::mma(ukf, tqf[ib][dc], f[ib]);
+          t[ib] = E::mma(vf, dof[ib][dc], t[ib]);
+          gg[ib] = E::mma(uvf, dof[ib][dc], gg[ib]);
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vp[jb][q] = p[q];
-        vds[jb][q] = p[q] * t[q];
-        vpf[jb][q] = p[q] * f[q];
-        vpw[jb][q] = p[q] * __builtin_fmaf(f[q], t[q], gg[q]);
+      for (int ib = 0; ib < NI; ++ib) {
+        f32x4 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[ib][q], c1, nl2[ib]));
+        if (edge) {
+          const int i = iw0 + 16 * ib + r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = j0 + 16 * jb + 4 * g + q;
+            if (j >= N || (CAUSAL && j > i)) p[q] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vp[ib][jb][q] = p[q];
+          vds[ib][jb][q] = p[q] * t[ib][q];
+          vpf[ib][jb][q] = p[q] * f[ib][q];
+          vpw[ib][jb][q] = p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]);
+        }
       }
     }
-    FBOB_SCHED_FENCE();
-    const F pB = E::from_f32(vp[0], vp[1]);
-    const F dsB = E::from_f32(vds[0], vds[1]);
-    const F pfB = E::from_f32(vpf[0], vpf[1]);
-    const F pwB = E::from_f32(vpw[0], vpw[1]);
-    accA = E::mma(ones, pfB, accA);
-    accE = E::mma(ones, pwB, accE);
+    if constexpr (FENCE) FBOB_SCHED_FENCE();
+    F pB[NI], dsB[NI], pfB[NI], pwB[NI];
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib) {
+      pB[ib] = E::from_f32(vp[ib][0], vp[ib][1]);
+      dsB[ib] = E::from_f32(vds[ib][0], vds[ib][1]);
+      pfB[ib] = E::from_f32(vpf[ib][0], vpf[ib][1]);
+      pwB[ib] = E::from_f32(vpw[ib][0], vpw[ib][1]);
+      accA[ib] = E::mma(ones, pfB[ib], accA[ib]);
+      accE[ib] = E::mma(ones, pwB[ib], accE[ib]);
+    }
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      FBOB_SCHED_FENCE();
+      if constexpr (FENCE) FBOB_SCHED_FENCE();
       const F kt = rd.tr(Kt, db);
       const F ukt = rd.tr(UKt, db);
       const F vt = rd.tr(Vt, db);
       const F uvt = rd.tr(UVt, db);
-      accB[db] = E::mma(kt, pB, accB[db]);
-      accX[db] = E::mma(kt, dsB, accX[db]);
-      accW[db] = E::mma(kt, pwB, accW[db]);
-      accW[db] = E::mma(ukt, dsB, accW[db]);
-      accO[db] = E::mma(vt, pfB, accO[db]);
-      accO[db] = E::mma(uvt, pB, accO[db]);
+#pragma unroll
+      for (int ib = 0; ib < NI; ++ib) {
+        accB[ib][db] = E::mma(kt, pB[ib], accB[ib][db]);
+        accX[ib][db] = E::mma(kt, dsB[ib], accX[ib][db]);
+        accW[ib][db] = E::mma(kt, pwB[ib], accW[ib][db]);
+        accW[ib][db] = E::mma(ukt, dsB[ib], accW[ib][db]);
+        accO[ib][db] = E::mma(vt, pfB[ib], accO[ib][db]);
+        accO[ib][db] = E::mma(uvt, pB[ib], accO[ib][db]);
+      }
     }
   };
 
@@ -171,7 +205,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     const int j0 = t * kBC;
     const bool more = t + 1 < ntc;
     if (more) st.load(j0 + kBC, N);
-    const bool active = !CAUSAL || j0 <= iw0 + 15;
+    const bool active = !CAUSAL || j0 <= iw0 + kRW - 1;
     if (active) tile(cur, j0);
     if (more) st.store(nxt);
     __syncthreads();
@@ -183,49 +217,63 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   }
 
   // ---- row correction and the single write of each row output ----
-  const float al = accA[0];  // F carries tau through the scaled resident operands
-  const float edeg = accE[0];
-  if (i < N) {
-    const int64_t ro = q_off + (int64_t)i * D;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const int d0 = 16 * db + 4 * g;
-      const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro + d0);
-      *reinterpret_cast<f32x4*>(a.ddOt + ro + d0) = accO[db] - al * o;
-      *reinterpret_cast<f32x4*>(a.dQt + ro + d0) =
-          tau * (accW[db] - al * accX[db] - edeg * accB[db]);
-    }
-    if (g == 0) {
-      a.alpha[(int64_t)bh * N + i] = al;
-      a.E[(int64_t)bh * N + i] = edeg - al * dv;
+  for (int ib = 0; ib < NI; ++ib) {
+    const int i = iw0 + 16 * ib + r;
+    const float al = accA[ib][0];  // F carries tau through the scaled resident operands
+    const float edeg = accE[ib][0];
+    if (i < N) {
+      const int64_t ro = q_off + (int64_t)i * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int d0 = 16 * db + 4 * g;
+        const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro + d0);
+        *reinterpret_cast<f32x4*>(a.ddOt + ro + d0) = accO[ib][db] - al * o;
+        *reinterpret_cast<f32x4*>(a.dQt + ro + d0) =
+            tau * (accW[ib][db] - al * accX[ib][db] - edeg * accB[ib][db]);
+      }
+      if (g == 0) {
+        a.alpha[(int64_t)bh * N + i] = al;
+        a.E[(int64_t)bh * N + i] = edeg - al * dv[ib];
+      }
     }
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NI, bool FENCE>
 hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
-  constexpr int kBR = NW * 16;
+  constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
   const int total = n_row_tiles * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, true>), dim3(total), dim3(NW * 64), 0, s, a, p.Hq,
-                       group, p.N, p.tau, n_row_tiles, total);
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, true>), dim3(total), dim3(NW * 64), 0, s,
+                       a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, false>), dim3(total), dim3(NW * 64), 0, s, a, p.Hq,
-                       group, p.N, p.tau, n_row_tiles, total);
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, false>), dim3(total), dim3(NW * 64), 0,
+                       s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
+}
+
+int tune_choice(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
 }
 
 }  // namespace
 
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.bf16) {
-    if (p.d == 64) return launch_t<__bf16, 64, 8>(p, a, s);
-    return launch_t<__bf16, 128, 4>(p, a, s);
+    if (p.d == 64) {
+      static const int cfg = tune_choice("FBOB_TUNE_P1");
+      if (cfg == 1) return launch_t<__bf16, 64, 4, 2, false>(p, a, s);
+      if (cfg == 2) return launch_t<__bf16, 64, 4, 2, true>(p, a, s);
+      return launch_t<__bf16, 64, 8, 1, true>(p, a, s);
+    }
+    return launch_t<__bf16, 128, 4, 1, true>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 4>(p, a, s);
-  return launch_t<float, 128, 4>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 1, true>(p, a, s);
+  return launch_t<float, 128, 4, 1, true>(p, a, s);
 }
 
 }  // namespace fbob
