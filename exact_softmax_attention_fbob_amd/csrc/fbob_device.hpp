@@ -15,6 +15,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace fbob {
@@ -298,6 +299,62 @@ struct MultiStager {
 };
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS staging (gfx950 global_load_lds_dwordx4): each
+// instruction moves 64 lanes x 16 bytes into 1 KiB of consecutive LDS (lane l at
+// byte 16 l), i.e. kRowsPerInst whole rows.  The XOR swizzle is applied on the
+// global side: the lane at physical chunk p of tile row `row` fetches logical
+// chunk p ^ swz(row).  No VGPRs hold the data and no ds_write is issued; the
+// caller waits on vmcnt before the barrier that publishes the tile.  Rows past
+// the end are clamped to the last row (finite data, given zero weight).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int ROWS, int NT, int NW>
+struct DirectStager {
+  static constexpr int kRB = Tile<T, D>::kRowBytes;
+  static constexpr int kChunks = Tile<T, D>::kChunks;
+  static constexpr int kRowsPerInst = 64 / kChunks;
+  static_assert(kRowsPerInst >= 1 && 64 % kChunks == 0, "rows must tile a 1 KiB block");
+  static constexpr int kInstPerTensor = ROWS / kRowsPerInst;
+  static constexpr int kInst = NT * kInstPerTensor;
+  static_assert(kInst % NW == 0, "staging instructions must divide evenly over waves");
+  static constexpr int kPer = kInst / NW;  // instructions per wave
+  static constexpr int kTileBytes = ROWS * kRB;
+  const char* src[kPer];  // tensor base + logical chunk column (per lane)
+  int row[kPer];          // tile row of this lane
+  int lds_off[kPer];      // wave-uniform LDS offset of the 1 KiB block
+
+  // w must be wave-uniform.
+  __device__ __forceinline__ void init(const T* const (&bases)[NT], int w, int lane) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int ii = k * NW + w;
+      const int tensor = ii / kInstPerTensor, rg = ii % kInstPerTensor;
+      row[k] = rg * kRowsPerInst + lane / kChunks;
+      const int c = (lane % kChunks) ^ Tile<T, D>::swz(row[k]);
+      const T* base = bases[0];
+#pragma unroll
+      for (int m = 1; m < NT; ++m)
+        if (tensor == m) base = bases[m];
+      src[k] = reinterpret_cast<const char*>(base) + c * 16;
+      lds_off[k] = tensor * kTileBytes + rg * 1024;
+    }
+  }
+  __device__ __forceinline__ void load(char* tiles, int row0, int nrows, int64_t byte_off = 0) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(1))) void glb_void;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int gr = min(row0 + row[k], nrows - 1);
+      const char* gp = src[k] + byte_off + (int64_t)gr * kRB;
+      __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)(tiles + lds_off[k]), 16, 0, 0);
+    }
+  }
+};
+
+// Wait for every outstanding memory operation of this wave (used before the
+// barrier that publishes tiles written by global_load_lds).
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------
 // Per-lane LDS fragment reader for 32-row staged tiles.  The swizzled byte
 // offsets that depend only on the lane are computed once; a read is then a
 // tile base plus a compile-time constant plus one of these registers.
@@ -362,6 +419,14 @@ __device__ __forceinline__ typename Elem<T>::frag scale_frag(typename Elem<T>::f
 }
 
 template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag zero_frag() {
+  typename Elem<T>::frag f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (T)0.0f;
+  return f;
+}
+
+template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag ones_frag() {
   typename Elem<T>::frag f;
 #pragma unroll
@@ -370,6 +435,12 @@ __device__ __forceinline__ typename Elem<T>::frag ones_frag() {
 }
 
 __device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
+
+// True when tau is an exact power of two, so that tau * x is exact in bf16.
+inline bool tau_is_pow2(float tau) {
+  int e = 0;
+  return tau > 0.f && frexpf(tau, &e) == 0.5f;
+}
 
 // Sum over the four 16-lane groups (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float group_sum(float x) {

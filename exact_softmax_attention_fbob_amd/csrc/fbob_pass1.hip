@@ -28,15 +28,16 @@
 // which leaves seven VALU operations plus one exp per score element.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
 namespace fbob {
 namespace {
 
-constexpr int kBC = 32;  // keys per LDS stage
-
-template <typename T, int D, int NW, int NI, bool FENCE, bool CAUSAL>
+template <typename T, int D, int NW, int NI, bool FENCE, bool TP2, bool SKEW, int BC, bool DIRECT,
+          bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
@@ -44,10 +45,12 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   constexpr int kThreads = NW * 64;
   constexpr int kRW = 16 * NI;                       // query rows per wave
   constexpr int kBR = NW * kRW;                      // query rows per work-group
+  constexpr int kBC = BC;                            // keys per LDS stage
   constexpr int kTB = kBC * Tile<T, D>::kRowBytes;   // bytes per staged tile
   constexpr int kDC = D / 32;
   constexpr int kDB = D / 16;
-  __shared__ __attribute__((aligned(16))) char lds[2][4 * kTB];
+  constexpr int kSlots = SKEW ? 3 : 2;  // LDS ring depth
+  __shared__ __attribute__((aligned(16))) char lds[kSlots][4 * kTB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -67,29 +70,35 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
 
   // ---- resident row operands (B operand of the transposed score tiles) ----
   const int iw0 = rt * kBR + w * kRW;
-  F qf[NI][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
+  // With TP2 (tau an exact power of two) tau Q is exact and also serves the
+  // score tile (S = (tau Q) K^T with exp2 scale log2 e); Q itself is not kept.
+  F qf[TP2 ? 1 : NI][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
   float nl2[NI], dv[NI];
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
     const int i = iw0 + 16 * ib + r;
 #pragma unroll
     for (int dc = 0; dc < kDC; ++dc) {
-      qf[ib][dc] = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
-      tqf[ib][dc] = scale_frag<T>(qf[ib][dc], tau);
+      const F q0 = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
+      if constexpr (!TP2) qf[ib][dc] = q0;
+      tqf[ib][dc] = scale_frag<T>(q0, tau);
       tuqf[ib][dc] = scale_frag<T>(global_frag(UQh, i, N, D, 32 * dc + 8 * g), tau);
       dof[ib][dc] = global_frag(dOh, i, N, D, 32 * dc + 8 * g);
     }
     nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
     dv[ib] = i < N ? a.D[(int64_t)bh * N + i] : 0.f;
   }
-  const F ones = ones_frag<T>();
+  // Row sums by MFMA: an operand of ones in rows 0..7 (for alpha) or rows 8..15
+  // (for E') makes C rows 0..7 hold sum_j P F and rows 8..15 sum_j P dP~'.  Lane
+  // (r, g) therefore holds alpha of row r for g < 2 and E' for g >= 2.
+  const F onesA = r < 8 ? ones_frag<T>() : zero_frag<T>();
+  const F onesE = r < 8 ? zero_frag<T>() : ones_frag<T>();
 
   f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
-  f32x4 accA[NI], accE[NI];  // alpha, E' (every q holds the row sum)
+  f32x4 accAE[NI];
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
-    accA[ib] = splat4(0.f);
-    accE[ib] = splat4(0.f);
+    accAE[ib] = splat4(0.f);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
       accB[ib][db] = splat4(0.f);
@@ -98,23 +107,27 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       accO[ib][db] = accB[ib][db];
     }
   }
-  const float c1 = tau * kLog2e;
+  const float c1 = TP2 ? kLog2e : tau * kLog2e;
   const LdsLane<T, D> rd(r, g);
 
   int jend = N;
   if (CAUSAL) jend = min(N, rt * kBR + kBR);
   const int ntc = (jend + kBC - 1) / kBC;
 
-  // One 32-key tile: scores, elementwise, contractions.  The bounds / causal
-  // test runs only on edge tiles (a wave-uniform branch around the P values).
-  auto tile = [&](const char* Kt, int j0) {
+  // Operand fragments of one 32-key tile for the contractions over keys.
+  struct Frags {
+    F p[NI], ds[NI], pf[NI], pw[NI];
+  };
+
+  // Scores and elementwise work of one 32-key tile, one 16-key block at a time;
+  // the K, V, U_K, U_V fragments of a block serve every row block of the wave.
+  // The bounds / causal test runs only on edge tiles (a wave-uniform branch
+  // around the P values).
+  auto score_phase = [&](const char* Kt, int j0, Frags& fr) {
     const char* Vt = Kt + kTB;
     const char* UKt = Kt + 2 * kTB;
     const char* UVt = Kt + 3 * kTB;
     const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > iw0);
-    // Scores and elementwise work one 16-key block at a time; the K, V, U_K, U_V
-    // fragments of a block serve every row block of the wave.
-    f32x4 vp[NI][2], vds[NI][2], vpf[NI][2], vpw[NI][2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       f32x4 s[NI], t[NI], f[NI], gg[NI];
@@ -133,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
         const F uvf = rd.row(UVt, jb, dc);
 #pragma unroll
         for (int ib = 0; ib < NI; ++ib) {
-          s[ib] = E::mma(kf, qf[ib][dc], s[ib]);
+          s[ib] = E::mma(kf, TP2 ? tqf[ib][dc] : qf[TP2 ? 0 : ib][dc], s[ib]);
           f[ib] = E::mma(kf, tuqf[ib][dc], f[ib]);
           f[ib] = E::mma(ukf, tqf[ib][dc], f[ib]);
           t[ib] = E::mma(vf, dof[ib][dc], t[ib]);
@@ -153,25 +166,28 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
             if (j >= N || (CAUSAL && j > i)) p[q] = 0.f;
           }
         }
+        // elements 4 jb .. 4 jb + 3 of the fragments
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          vp[ib][jb][q] = p[q];
-          vds[ib][jb][q] = p[q] * t[ib][q];
-          vpf[ib][jb][q] = p[q] * f[ib][q];
-          vpw[ib][jb][q] = p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]);
+          fr.p[ib][4 * jb + q] = (T)p[q];
+          fr.ds[ib][4 * jb + q] = (T)(p[q] * t[ib][q]);
+          fr.pf[ib][4 * jb + q] = (T)(p[q] * f[ib][q]);
+          fr.pw[ib][4 * jb + q] = (T)(p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]));
         }
       }
     }
+  };
+
+  // Contractions over the tile's keys (transposed outputs) and the row sums.
+  auto output_phase = [&](const char* Kt, const Frags& fr) {
+    const char* Vt = Kt + kTB;
+    const char* UKt = Kt + 2 * kTB;
+    const char* UVt = Kt + 3 * kTB;
     if constexpr (FENCE) FBOB_SCHED_FENCE();
-    F pB[NI], dsB[NI], pfB[NI], pwB[NI];
 #pragma unroll
     for (int ib = 0; ib < NI; ++ib) {
-      pB[ib] = E::from_f32(vp[ib][0], vp[ib][1]);
-      dsB[ib] = E::from_f32(vds[ib][0], vds[ib][1]);
-      pfB[ib] = E::from_f32(vpf[ib][0], vpf[ib][1]);
-      pwB[ib] = E::from_f32(vpw[ib][0], vpw[ib][1]);
-      accA[ib] = E::mma(ones, pfB[ib], accA[ib]);
-      accE[ib] = E::mma(ones, pwB[ib], accE[ib]);
+      accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
+      accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
     }
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
@@ -182,46 +198,109 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       const F uvt = rd.tr(UVt, db);
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
-        accB[ib][db] = E::mma(kt, pB[ib], accB[ib][db]);
-        accX[ib][db] = E::mma(kt, dsB[ib], accX[ib][db]);
-        accW[ib][db] = E::mma(kt, pwB[ib], accW[ib][db]);
-        accW[ib][db] = E::mma(ukt, dsB[ib], accW[ib][db]);
-        accO[ib][db] = E::mma(vt, pfB[ib], accO[ib][db]);
-        accO[ib][db] = E::mma(uvt, pB[ib], accO[ib][db]);
+        accB[ib][db] = E::mma(kt, fr.p[ib], accB[ib][db]);
+        accX[ib][db] = E::mma(kt, fr.ds[ib], accX[ib][db]);
+        accW[ib][db] = E::mma(kt, fr.pw[ib], accW[ib][db]);
+        accW[ib][db] = E::mma(ukt, fr.ds[ib], accW[ib][db]);
+        accO[ib][db] = E::mma(vt, fr.pf[ib], accO[ib][db]);
+        accO[ib][db] = E::mma(uvt, fr.p[ib], accO[ib][db]);
       }
     }
   };
 
-  MultiStager<T, D, kBC, 4, kThreads> st;
-  st.init(kv_bases, tid);
-  st.load(0, N);
-  st.store(lds[0]);
+  // Staging: registers + ds_write (MultiStager) or direct global -> LDS.
+  using RegStager = MultiStager<T, D, kBC, 4, kThreads>;
+  using DirStager = DirectStager<T, D, kBC, 4, NW>;
+  typename std::conditional<DIRECT, DirStager, RegStager>::type st;
+  auto stage_init = [&]() {
+    if constexpr (DIRECT) st.init(kv_bases, w, lane);
+    else st.init(kv_bases, tid);
+  };
+  // Issue the loads of the tile at key j0 (into `buf` when DIRECT).
+  auto stage_load = [&](char* buf, int j0) {
+    if constexpr (DIRECT) st.load(buf, j0, N);
+    else st.load(j0, N);
+  };
+  // Make the staged tile visible in `buf` (the barrier follows).
+  auto stage_commit = [&](char* buf) {
+    if constexpr (DIRECT) wait_all_memory();
+    else st.store(buf);
+  };
+  stage_init();
+  stage_load(lds[0], 0);
+  stage_commit(lds[0]);
   __syncthreads();
 
-  // One pipeline step: prefetch tile t+1 into registers, compute tile t from
-  // `cur`, store tile t+1 into `nxt`, barrier.  Unrolled by two so that both
-  // LDS buffers are compile-time addresses.
-  auto step = [&](int t, char* cur, char* nxt) {
-    const int j0 = t * kBC;
-    const bool more = t + 1 < ntc;
-    if (more) st.load(j0 + kBC, N);
-    const bool active = !CAUSAL || j0 <= iw0 + kRW - 1;
-    if (active) tile(cur, j0);
-    if (more) st.store(nxt);
-    __syncthreads();
+  auto active_tile = [&](int t) { return !CAUSAL || t * kBC <= iw0 + kRW - 1; };
+  // Both 32-key halves of a stage (BC = 64) or the single one (BC = 32).
+  auto compute_stage = [&](const char* cur, int j0) {
+#pragma unroll
+    for (int hs = 0; hs < kBC / 32; ++hs) {
+      const int js = j0 + 32 * hs;
+      if (!CAUSAL || js <= iw0 + kRW - 1) {
+        Frags fr;
+        score_phase(cur + 32 * hs * Tile<T, D>::kRowBytes, js, fr);
+        output_phase(cur + 32 * hs * Tile<T, D>::kRowBytes, fr);
+      }
+    }
   };
+
+  if constexpr (!SKEW) {
+    // One pipeline step: prefetch tile t+1, compute tile t from `cur`, publish
+    // tile t+1 in `nxt`, barrier.  Unrolled by two so that both LDS buffers are
+    // compile-time addresses.
+    auto step = [&](int t, char* cur, char* nxt) {
+      const int j0 = t * kBC;
+      const bool more = t + 1 < ntc;
+      if (more) stage_load(nxt, j0 + kBC);
+      if (active_tile(t)) compute_stage(cur, j0);
+      if (more) stage_commit(nxt);
+      __syncthreads();
+    };
 #pragma unroll 1
-  for (int t = 0; t < ntc; t += 2) {
-    step(t, lds[0], lds[1]);
-    if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
+    for (int t = 0; t < ntc; t += 2) {
+      step(t, lds[0], lds[1]);
+      if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
+    }
+  } else {
+    // Phase-skewed schedule.  The two waves sharing a SIMD (w and w + NW/2) run
+    // half a tile apart: the late group contracts tile t-1 while it builds the
+    // fragments of tile t, so one wave's elementwise work overlaps the other's
+    // contractions.  A three-slot LDS ring keeps tile t-1 resident for it.
+    const bool late = w >= NW / 2;
+    Frags held;
+    static_assert(!SKEW || BC == 32, "the skewed schedule works on 32-key stages");
+    auto step = [&](int t, const char* prev, char* cur, char* nxt) {
+      const int j0 = t * kBC;
+      const bool more = t + 1 < ntc;
+      if (more) stage_load(nxt, j0 + kBC);
+      if (late) {
+        if (t > 0 && active_tile(t - 1)) output_phase(prev, held);
+        if (active_tile(t)) score_phase(cur, j0, held);
+      } else if (active_tile(t)) {
+        Frags fr;
+        score_phase(cur, j0, fr);
+        output_phase(cur, fr);
+      }
+      if (more) stage_commit(nxt);
+      __syncthreads();
+    };
+#pragma unroll 1
+    for (int t = 0; t < ntc; t += 3) {
+      step(t, lds[2], lds[0], lds[1]);
+      if (t + 1 < ntc) step(t + 1, lds[0], lds[1], lds[2]);
+      if (t + 2 < ntc) step(t + 2, lds[1], lds[2], lds[0]);
+    }
+    if (late && active_tile(ntc - 1)) output_phase(lds[(ntc - 1) % 3], held);
   }
 
   // ---- row correction and the single write of each row output ----
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
     const int i = iw0 + 16 * ib + r;
-    const float al = accA[ib][0];  // F carries tau through the scaled resident operands
-    const float edeg = accE[ib][0];
+    // F carries tau through the scaled resident operands.
+    const float al = __shfl(accAE[ib][0], r);
+    const float edeg = __shfl(accAE[ib][0], 32 + r);
     if (i < N) {
       const int64_t ro = q_off + (int64_t)i * D;
 #pragma unroll
@@ -240,17 +319,18 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   }
 }
 
-template <typename T, int D, int NW, int NI, bool FENCE>
+template <typename T, int D, int NW, int NI, bool FENCE, bool TP2, bool SKEW = false, int BC = 32,
+          bool DIRECT = false>
 hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
   const int total = n_row_tiles * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, true>), dim3(total), dim3(NW * 64), 0, s,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TP2, SKEW, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,
                        a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, false>), dim3(total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TP2, SKEW, BC, DIRECT, false>), dim3(total), dim3(NW * 64), 0,
                        s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
 }
@@ -266,14 +346,18 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.bf16) {
     if (p.d == 64) {
       static const int cfg = tune_choice("FBOB_TUNE_P1");
-      if (cfg == 1) return launch_t<__bf16, 64, 4, 2, false>(p, a, s);
-      if (cfg == 2) return launch_t<__bf16, 64, 4, 2, true>(p, a, s);
-      return launch_t<__bf16, 64, 8, 1, true>(p, a, s);
+      if (tau_is_pow2(p.tau)) {
+        if (cfg == 1) return launch_t<__bf16, 64, 8, 1, true, true, false, 32, true>(p, a, s);
+        if (cfg == 2) return launch_t<__bf16, 64, 8, 1, true, true, false, 32, false>(p, a, s);
+        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, false, true, false, 64, true>(p, a, s);
+        return launch_t<__bf16, 64, 8, 1, true, true, false, 64, true>(p, a, s);
+      }
+      return launch_t<__bf16, 64, 8, 1, true, false>(p, a, s);
     }
-    return launch_t<__bf16, 128, 4, 1, true>(p, a, s);
+    return launch_t<__bf16, 128, 4, 1, true, false>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 4, 1, true>(p, a, s);
-  return launch_t<float, 128, 4, 1, true>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 1, true, false>(p, a, s);
+  return launch_t<float, 128, 4, 1, true, false>(p, a, s);
 }
 
 }  // namespace fbob

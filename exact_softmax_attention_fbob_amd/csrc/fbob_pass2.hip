@@ -26,19 +26,24 @@
 // index on the MFMA row axis, so a lane owns one key and four consecutive rows
 // per block; those C registers are directly the B operand of the contractions
 // over rows, whose A operand (Q^T, U_Q^T, dO^T) comes from transposed LDS reads.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
 namespace fbob {
 namespace {
 
-template <typename T, int D, int NW, int BRS, bool CAUSAL>
+template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, bool TP2, bool DIRECT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
                                                         float tau, int n_col_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int kThreads = NW * 64;
-  constexpr int kBCw = NW * 16;                     // keys per work-group
+  constexpr int kCW = 16 * NJ;                      // keys per wave
+  constexpr int kBCw = NW * kCW;                    // keys per work-group
   constexpr int kTB = BRS * Tile<T, D>::kRowBytes;  // bytes per staged tile
   constexpr int kDC = D / 32;
   constexpr int kDB = D / 16;
@@ -59,26 +64,32 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   const T* UKh = reinterpret_cast<const T*>(a.UK) + kv_off;
   const T* UVh = reinterpret_cast<const T*>(a.UV) + kv_off;
 
-  const int jw0 = ct * kBCw + w * 16;
-  const int j = jw0 + r;  // this lane's key
-  F kf[kDC], tkf[kDC], tukf[kDC], vf[kDC], uvf[kDC];
+  const int jw0 = ct * kBCw + w * kCW;
+  // With TP2 (tau an exact power of two) tau K is exact, so the score tile also
+  // uses it (S = Q (tau K)^T with exp2 scale log2 e) and K itself is not kept.
+  F kf[TP2 ? 1 : NJ][kDC], tkf[NJ][kDC], tukf[NJ][kDC], vf[NJ][kDC], uvf[NJ][kDC];
 #pragma unroll
-  for (int dc = 0; dc < kDC; ++dc) {
-    const int col = 32 * dc + 8 * g;
-    kf[dc] = global_frag(Kh, j, N, D, col);
-    tkf[dc] = scale_frag<T>(kf[dc], tau);
-    tukf[dc] = scale_frag<T>(global_frag(UKh, j, N, D, col), tau);
-    vf[dc] = global_frag(Vh, j, N, D, col);
-    uvf[dc] = global_frag(UVh, j, N, D, col);
-  }
+  for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+    for (int dc = 0; dc < kDC; ++dc) {
+      const int j = jw0 + 16 * jb + r, col = 32 * dc + 8 * g;
+      const F k0 = global_frag(Kh, j, N, D, col);
+      if constexpr (!TP2) kf[jb][dc] = k0;
+      tkf[jb][dc] = scale_frag<T>(k0, tau);
+      tukf[jb][dc] = scale_frag<T>(global_frag(UKh, j, N, D, col), tau);
+      vf[jb][dc] = global_frag(Vh, j, N, D, col);
+      uvf[jb][dc] = global_frag(UVh, j, N, D, col);
+    }
 
-  f32x4 accK[kDB], accV[kDB];
+  f32x4 accK[NJ][kDB], accV[NJ][kDB];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) {
-    accK[db] = splat4(0.f);
-    accV[db] = accK[db];
-  }
-  const float c1 = tau * kLog2e;
+  for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      accK[jb][db] = splat4(0.f);
+      accV[jb][db] = accK[jb][db];
+    }
+  const float c1 = TP2 ? kLog2e : tau * kLog2e;
   const LdsLane<T, D> rd(r, g);
 
   // Row steps: (query head of the group, row chunk); causal rows start at the
@@ -92,15 +103,21 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   const T* const q_bases[3] = {reinterpret_cast<const T*>(a.Q) + q0,
                                reinterpret_cast<const T*>(a.dO) + q0,
                                reinterpret_cast<const T*>(a.UQ) + q0};
-  MultiStager<T, D, BRS, 3, kThreads> st;
-  st.init(q_bases, tid);
+  // Q, dO, U_Q tiles: registers + ds_write (MultiStager) or direct global -> LDS.
+  using RegStager = MultiStager<T, D, BRS, 3, kThreads>;
+  using DirStager = DirectStager<T, D, BRS, 3, NW>;
+  typename std::conditional<DIRECT, DirStager, RegStager>::type st;
+  if constexpr (DIRECT) st.init(q_bases, w, lane);
+  else st.init(q_bases, tid);
   // Row scalars: thread tid < BRS stages row tid of the chunk.
   const int64_t s0 = ((int64_t)b * Hq + (int64_t)hk * group) * N;
   f32x4 scal = splat4(0.f);
-  auto load_step = [&](int step) {
+  // Issue the loads of step `step` (tiles go straight into `buf` when DIRECT).
+  auto load_step = [&](int step, char* buf) {
     const int hq = step / nrc;
     const int i0 = i_begin + (step % nrc) * BRS;
-    st.load(i0, N, hq * q_head);
+    if constexpr (DIRECT) st.load(buf, i0, N, hq * q_head);
+    else st.load(i0, N, hq * q_head);
     if (tid < BRS) {
       const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
       const float L = a.L[ri], Dv = a.D[ri], al = a.alpha[ri], Ev = a.E[ri];
@@ -108,7 +125,8 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
     }
   };
   auto store_step = [&](char* buf) {
-    st.store(buf);
+    if constexpr (DIRECT) wait_all_memory();
+    else st.store(buf);
     if (tid < BRS) {
       float* sp = reinterpret_cast<float*>(buf + 3 * kTB);
 #pragma unroll
@@ -123,71 +141,85 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
     const char* UQt = buf + 2 * kTB;
     const float* sp = reinterpret_cast<const float*>(buf + 3 * kTB);
     const int ic = i0 + 32 * sc;
-    const bool edge = (ic + 32 > N) || (CAUSAL && ic < jw0 + 15);
-    f32x4 vds[2], vddp[2], vdst[2];
+    const bool edge = (ic + 32 > N) || (CAUSAL && ic < jw0 + kCW - 1);
+    F dsB[NJ], ddpB[NJ], dstB[NJ];  // filled half by half: elements 4 ib .. 4 ib + 3
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       const int rr = 32 * sc + 16 * ib + 4 * g;  // first of this lane's 4 rows in the tile
       const f32x4 nL = *reinterpret_cast<const f32x4*>(sp + rr);
-      f32x4 s = splat4(0.f);
-      f32x4 t = *reinterpret_cast<const f32x4*>(sp + BRS + rr);
-      f32x4 u = *reinterpret_cast<const f32x4*>(sp + 2 * BRS + rr);
-      f32x4 gp = *reinterpret_cast<const f32x4*>(sp + 3 * BRS + rr);
+      const f32x4 nD = *reinterpret_cast<const f32x4*>(sp + BRS + rr);
+      const f32x4 nA = *reinterpret_cast<const f32x4*>(sp + 2 * BRS + rr);
+      const f32x4 nG = *reinterpret_cast<const f32x4*>(sp + 3 * BRS + rr);
+      f32x4 s[NJ], t[NJ], u[NJ], gp[NJ];
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        s[jb] = splat4(0.f);
+        t[jb] = nD;
+        u[jb] = nA;
+        gp[jb] = nG;
+      }
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
         const F qa = rd.row(Qt, 2 * sc + ib, dc);
         const F doa = rd.row(dOt, 2 * sc + ib, dc);
         const F uqa = rd.row(UQt, 2 * sc + ib, dc);
-        s = E::mma(qa, kf[dc], s);
-        u = E::mma(uqa, tkf[dc], u);
-        u = E::mma(qa, tukf[dc], u);
-        t = E::mma(doa, vf[dc], t);
-        gp = E::mma(doa, uvf[dc], gp);
-      }
-      f32x4 p;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[q], c1, nL[q]));
-      if (edge) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = ic + 16 * ib + 4 * g + q;
-          if (i >= N || (CAUSAL && j > i)) p[q] = 0.f;
+        for (int jb = 0; jb < NJ; ++jb) {
+          s[jb] = E::mma(qa, TP2 ? tkf[jb][dc] : kf[TP2 ? 0 : jb][dc], s[jb]);
+          u[jb] = E::mma(uqa, tkf[jb][dc], u[jb]);
+          u[jb] = E::mma(qa, tukf[jb][dc], u[jb]);
+          t[jb] = E::mma(doa, vf[jb][dc], t[jb]);
+          gp[jb] = E::mma(doa, uvf[jb][dc], gp[jb]);
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vds[ib][q] = p[q] * t[q];
-        vddp[ib][q] = p[q] * u[q];
-        vdst[ib][q] = p[q] * __builtin_fmaf(u[q], t[q], gp[q]);
+      for (int jb = 0; jb < NJ; ++jb) {
+        f32x4 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[jb][q], c1, nL[q]));
+        if (edge) {
+          const int j = jw0 + 16 * jb + r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = ic + 16 * ib + 4 * g + q;
+            if (i >= N || (CAUSAL && j > i)) p[q] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          dsB[jb][4 * ib + q] = (T)(p[q] * t[jb][q]);
+          ddpB[jb][4 * ib + q] = (T)(p[q] * u[jb][q]);
+          dstB[jb][4 * ib + q] = (T)(p[q] * __builtin_fmaf(u[jb][q], t[jb][q], gp[jb][q]));
+        }
       }
     }
-    FBOB_SCHED_FENCE();
-    const F dsB = E::from_f32(vds[0], vds[1]);
-    const F ddpB = E::from_f32(vddp[0], vddp[1]);
-    const F dstB = E::from_f32(vdst[0], vdst[1]);
+    if constexpr (FENCE) FBOB_SCHED_FENCE();
     const char* Qs = Qt + 32 * sc * Tile<T, D>::kRowBytes;
     const char* dOs = dOt + 32 * sc * Tile<T, D>::kRowBytes;
     const char* UQs = UQt + 32 * sc * Tile<T, D>::kRowBytes;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      FBOB_SCHED_FENCE();
+      if constexpr (FENCE) FBOB_SCHED_FENCE();
       const F qt = rd.tr(Qs, db);
       const F uqt = rd.tr(UQs, db);
       const F dot = rd.tr(dOs, db);
-      accK[db] = E::mma(qt, dstB, accK[db]);
-      accK[db] = E::mma(uqt, dsB, accK[db]);
-      accV[db] = E::mma(dot, ddpB, accV[db]);
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        accK[jb][db] = E::mma(qt, dstB[jb], accK[jb][db]);
+        accK[jb][db] = E::mma(uqt, dsB[jb], accK[jb][db]);
+        accV[jb][db] = E::mma(dot, ddpB[jb], accV[jb][db]);
+      }
     }
   };
 
-  load_step(0);
+  load_step(0, lds[0]);
   store_step(lds[0]);
   __syncthreads();
 
   auto step = [&](int t, char* cur, char* nxt) {
     const int i0 = i_begin + (t % nrc) * BRS;
     const bool more = t + 1 < nsteps;
-    if (more) load_step(t + 1);
+    if (more) load_step(t + 1, nxt);
 #pragma unroll
     for (int sc = 0; sc < BRS / 32; ++sc) {
       const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
@@ -203,41 +235,59 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   }
 
   // ---- single exclusive write of dK~ and dV~ ----
-  if (j < N) {
-    const int64_t ro = kv_off + (int64_t)j * D;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const int d0 = 16 * db + 4 * g;
-      *reinterpret_cast<f32x4*>(a.dKt + ro + d0) = tau * accK[db];
-      *reinterpret_cast<f32x4*>(a.dVt + ro + d0) = accV[db];
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int j = jw0 + 16 * jb + r;
+    if (j < N) {
+      const int64_t ro = kv_off + (int64_t)j * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int d0 = 16 * db + 4 * g;
+        *reinterpret_cast<f32x4*>(a.dKt + ro + d0) = tau * accK[jb][db];
+        *reinterpret_cast<f32x4*>(a.dVt + ro + d0) = accV[jb][db];
+      }
     }
   }
 }
 
-template <typename T, int D, int NW, int BRS>
+template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, bool TP2, bool DIRECT = false>
 hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
-  constexpr int kBCw = NW * 16;
+  constexpr int kBCw = NW * 16 * NJ;
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
   const int total = n_col_tiles * p.B * p.Hkv;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass2_kernel<T, D, NW, BRS, true>), dim3(total), dim3(NW * 64), 0, s, a,
-                       p.Hkv, group, p.N, p.tau, n_col_tiles, total);
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TP2, DIRECT, true>), dim3(total), dim3(NW * 64),
+                       0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   else
-    hipLaunchKernelGGL((pass2_kernel<T, D, NW, BRS, false>), dim3(total), dim3(NW * 64), 0, s, a,
-                       p.Hkv, group, p.N, p.tau, n_col_tiles, total);
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TP2, DIRECT, false>), dim3(total), dim3(NW * 64),
+                       0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   return hipGetLastError();
+}
+
+int tune_choice(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
 }
 
 }  // namespace
 
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
   if (p.bf16) {
-    if (p.d == 64) return launch_t<__bf16, 64, 8, 64>(p, a, s);
-    return launch_t<__bf16, 128, 4, 32>(p, a, s);
+    if (p.d == 64) {
+      static const int cfg = tune_choice("FBOB_TUNE_P2");
+      if (tau_is_pow2(p.tau)) {
+        if (cfg == 1) return launch_t<__bf16, 64, 8, 2, 64, false, true, false>(p, a, s);
+        if (cfg == 2) return launch_t<__bf16, 64, 8, 2, 64, true, true, true>(p, a, s);
+        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 64, true, true, false>(p, a, s);
+        return launch_t<__bf16, 64, 8, 2, 64, false, true, true>(p, a, s);
+      }
+      return launch_t<__bf16, 64, 8, 1, 64, true, false>(p, a, s);
+    }
+    return launch_t<__bf16, 128, 4, 1, 32, true, false>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 4, 32>(p, a, s);
-  return launch_t<float, 128, 4, 32>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 1, 32, true, false>(p, a, s);
+  return launch_t<float, 128, 4, 1, 32, true, false>(p, a, s);
 }
 
 }  // namespace fbob
