@@ -131,7 +131,7 @@ def main():
     p.add_argument("--launches", type=int, default=3)
     p = sub.add_parser("record")
     p.add_argument("--kernel", default="pass1_kernel")
-    p.add_argument("--copy-kernel", default="elementwise")
+    p.add_argument("--copy-kernel", default="copyBuffer")
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)
     p.add_argument("--copy-fetch", required=True)
