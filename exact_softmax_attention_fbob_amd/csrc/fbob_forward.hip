@@ -5,34 +5,38 @@
 // FlashAttention blog ("FlashAttention 的反向传播设计"), sections 一 and 二: the
 // forward keeps only per-row statistics; FlashBoB notes, "关键设计" 1: D_i.
 //
-// Schedule: one work-group = 4 waves, each wave owns 16*NI query rows that stay
-// in registers (Q as MFMA operand, O as fp32 accumulator).  K and V column tiles
-// of 32 keys are staged through LDS, double-buffered.  Scores are computed
-// transposed (S^T = K Q^T), so a lane owns one query row and 8 keys of the tile;
-// the row maximum needs one cross-group reduction per tile, the row sum is kept
-// per lane and reduced once at the end (online softmax with exp2).
+// Schedule: one work-group = NW waves, each wave owns 16 query rows (Q as MFMA
+// operand, O as fp32 accumulator in registers).  K and V tiles of BC keys are
+// staged straight into LDS (double-buffered).  Scores are computed transposed
+// (S^T = K Q^T), so a lane owns one query row and 8 keys per 32-key block.
+// Online softmax in base 2 with a lazy running maximum: the weights are
+// exp2(x - m) for a per-row reference m that is raised only when a row's new
+// maximum exceeds it by more than kSlack (weights then stay <= 2^kSlack), so the
+// accumulator rescale is rare.  The row sum of the weights is an MFMA contraction
+// with a ones operand over the same bf16 weights that multiply V.
+#include <type_traits>
+
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
 namespace fbob {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBC = 32;  // keys per LDS stage
+constexpr float kSlack = 8.0f;  // log2 headroom before the reference max is raised
 
-template <typename T, int D, int NI, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a, int Hq, int group, int N,
-                                                       float tau, int n_row_tiles, int total) {
+template <typename T, int D, int NW, int BC, bool TP2, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int group, int N,
+                                                      float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int kRowsW = 16 * NI;
-  constexpr int kBR = 4 * kRowsW;
-  constexpr int kTB = kBC * Tile<T, D>::kRowBytes;  // bytes per staged tile
-  constexpr int kDC = D / 32;                        // 32-wide d chunks
-  constexpr int kDB = D / 16;                        // 16-wide d blocks
+  constexpr int kBR = NW * 16;
+  constexpr int kTB = BC * Tile<T, D>::kRowBytes;  // bytes per staged tile
+  constexpr int kDC = D / 32;
+  constexpr int kDB = D / 16;
   __shared__ __attribute__((aligned(16))) char lds[2][2 * kTB];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
   const int bh = logical / n_row_tiles, rt = logical % n_row_tiles;
@@ -40,150 +44,135 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a, int Hq, int gr
   const int64_t q_off = (int64_t)bh * N * D;
   const int64_t kv_off = ((int64_t)b * (Hq / group) + hk) * N * D;
   const T* Qh = reinterpret_cast<const T*>(a.Q) + q_off;
-  const T* Kh = reinterpret_cast<const T*>(a.K) + kv_off;
-  const T* Vh = reinterpret_cast<const T*>(a.V) + kv_off;
   const T* dOh = reinterpret_cast<const T*>(a.dO) + q_off;
+  const T* const kv_bases[2] = {reinterpret_cast<const T*>(a.K) + kv_off,
+                                reinterpret_cast<const T*>(a.V) + kv_off};
 
-  const int iw0 = rt * kBR + w * kRowsW;
-  F qf[NI][kDC];
+  const int iw0 = rt * kBR + w * 16;
+  const int i = iw0 + r;  // this lane's query row
+  // With TP2 (tau an exact power of two) the score operand is tau Q (exact).
+  F qf[kDC];
 #pragma unroll
-  for (int ib = 0; ib < NI; ++ib)
-#pragma unroll
-    for (int dc = 0; dc < kDC; ++dc) qf[ib][dc] = global_frag(Qh, iw0 + 16 * ib + r, N, D, 32 * dc + 8 * g);
-
-  f32x4 acc[NI][kDB];
-  float m[NI], l[NI];
-#pragma unroll
-  for (int ib = 0; ib < NI; ++ib) {
-    m[ib] = -INFINITY;
-    l[ib] = 0.f;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) acc[ib][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dc = 0; dc < kDC; ++dc) {
+    const F q0 = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
+    qf[dc] = TP2 ? scale_frag<T>(q0, tau) : q0;
   }
-  const float c1 = tau * kLog2e;
+  const float c1 = TP2 ? kLog2e : tau * kLog2e;
+  const F ones = ones_frag<T>();
+
+  f32x4 acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) acc[db] = splat4(0.f);
+  f32x4 accL = splat4(0.f);  // row sum of the weights (every q holds it)
+  float m = -INFINITY;       // reference maximum of this lane's row (log2 units)
+  const LdsLane<T, D> rd(r, g);
 
   int jend = N;
   if (CAUSAL) jend = min(N, rt * kBR + kBR);
-  const int ntc = (jend + kBC - 1) / kBC;
+  const int ntc = (jend + BC - 1) / BC;
 
-  Stager<T, D, kBC, kThreads> sk, sv;
-  sk.load(Kh, 0, N, tid);
-  sv.load(Vh, 0, N, tid);
-  sk.store(lds[0], tid);
-  sv.store(lds[0] + kTB, tid);
+  // 32 keys of a staged tile.
+  auto block32 = [&](const char* Kt, const char* Vt, int j0) {
+    const bool edge = (j0 + 32 > N) || (CAUSAL && j0 + 31 > iw0);
+    // Raw scores; the row maximum is taken before scaling (c1 > 0 commutes with
+    // max), so each weight costs one FMA and one exp2.
+    f32x4 s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      s[jb] = splat4(0.f);
+#pragma unroll
+      for (int dc = 0; dc < kDC; ++dc) s[jb] = E::mma(rd.row(Kt, jb, dc), qf[dc], s[jb]);
+      if (edge) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + 16 * jb + 4 * g + q;
+          if (j >= N || (CAUSAL && j > i)) s[jb][q] = -INFINITY;
+        }
+      }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mt = group_max(mt) * c1;
+    // Raise the reference only when the new maximum would push a weight above
+    // 2^kSlack (always on the first block, where m = -inf).
+    if (__any(mt > m + kSlack)) {
+      const float mn = fmaxf(m, mt);
+      const float sc = fast_exp2(m - mn);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) acc[db] *= sc;
+      accL *= sc;
+      m = mn;
+    }
+    const float nm = -m;
+    F pB;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pB[4 * jb + q] = (T)fast_exp2(__builtin_fmaf(s[jb][q], c1, nm));
+    accL = E::mma(ones, pB, accL);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) acc[db] = E::mma(rd.tr(Vt, db), pB, acc[db]);
+  };
+
+  DirectStager<T, D, BC, 2, NW> st;
+  st.init(kv_bases, w, lane);
+  st.load(lds[0], 0, N);
+  wait_all_memory();
   __syncthreads();
 
-  for (int t = 0; t < ntc; ++t) {
-    const int j0 = t * kBC;
+  auto step = [&](int t, char* cur, char* nxt) {
+    const int j0 = t * BC;
     const bool more = t + 1 < ntc;
-    if (more) {
-      sk.load(Kh, j0 + kBC, N, tid);
-      sv.load(Vh, j0 + kBC, N, tid);
+    if (more) st.load(nxt, j0 + BC, N);
+#pragma unroll
+    for (int hs = 0; hs < BC / 32; ++hs) {
+      const int js = j0 + 32 * hs;
+      if (!CAUSAL || js <= iw0 + 15)
+        block32(cur + 32 * hs * Tile<T, D>::kRowBytes,
+                cur + kTB + 32 * hs * Tile<T, D>::kRowBytes, js);
     }
-    const char* Kt = lds[t & 1];
-    const char* Vt = Kt + kTB;
-    const bool active = !CAUSAL || j0 <= iw0 + kRowsW - 1;
-    if (active) {
-      f32x4 s[2][NI];
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int ib = 0; ib < NI; ++ib) s[jb][ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int dc = 0; dc < kDC; ++dc) {
-          const F kf = lds_frag_row<T, D>(Kt, 16 * jb + r, 32 * dc + 8 * g);
-#pragma unroll
-          for (int ib = 0; ib < NI; ++ib) s[jb][ib] = E::mma(kf, qf[ib][dc], s[jb][ib]);
-        }
-      const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > iw0);
-      F pf[NI];
-#pragma unroll
-      for (int ib = 0; ib < NI; ++ib) {
-        const int i = iw0 + 16 * ib + r;
-        float mt = -INFINITY;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float x = s[jb][ib][q] * c1;
-            if (edge) {
-              const int j = j0 + 16 * jb + 4 * g + q;
-              if (j >= N || (CAUSAL && j > i)) x = -INFINITY;
-            }
-            s[jb][ib][q] = x;
-            mt = fmaxf(mt, x);
-          }
-        mt = group_max(mt);
-        const float mn = fmaxf(m[ib], mt);
-        const float sc = fast_exp2(m[ib] - mn);
-        m[ib] = mn;
-        float ls = 0.f;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float p = fast_exp2(s[jb][ib][q] - mn);
-            s[jb][ib][q] = p;
-            ls += p;
-          }
-        l[ib] = l[ib] * sc + ls;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) acc[ib][db] *= sc;
-        pf[ib] = E::from_f32(s[0][ib], s[1][ib]);
-      }
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const F vt = lds_frag_tr<T, D>(Vt, 0, 16 * db, r, g);
-#pragma unroll
-        for (int ib = 0; ib < NI; ++ib) acc[ib][db] = E::mma(vt, pf[ib], acc[ib][db]);
-      }
-    }
-    if (more) {
-      sk.store(lds[(t + 1) & 1], tid);
-      sv.store(lds[(t + 1) & 1] + kTB, tid);
-    }
+    if (more) wait_all_memory();
     __syncthreads();
+  };
+#pragma unroll 1
+  for (int t = 0; t < ntc; t += 2) {
+    step(t, lds[0], lds[1]);
+    if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
   }
 
-  // Epilogue: O = acc / l, L = ln(sum) + max, D = dO . O (fp32 O).
+  // Epilogue: O = acc / l, L = (m + log2 l) ln 2, D = dO . O (fp32 O).
+  const float lsum = accL[0];
+  const float inv = 1.f / lsum;
+  float dpart = 0.f;
+  if (i < N) {
 #pragma unroll
-  for (int ib = 0; ib < NI; ++ib) {
-    const int i = iw0 + 16 * ib + r;
-    const float lsum = group_sum(l[ib]);
-    const float inv = 1.f / lsum;
-    float dpart = 0.f;
-    if (i < N) {
+    for (int db = 0; db < kDB; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      const f32x4 o = acc[db] * inv;
+      *reinterpret_cast<f32x4*>(a.O + q_off + (int64_t)i * D + d0) = o;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const int d0 = 16 * db + 4 * g;
-        const f32x4 o = acc[ib][db] * inv;
-        *reinterpret_cast<f32x4*>(a.O + q_off + (int64_t)i * D + d0) = o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dpart += (float)dOh[(int64_t)i * D + d0 + q] * o[q];
-      }
+      for (int q = 0; q < 4; ++q) dpart += (float)dOh[(int64_t)i * D + d0 + q] * o[q];
     }
-    const float dsum = group_sum(dpart);
-    if (i < N && g == 0) {
-      a.L[(int64_t)bh * N + i] = (m[ib] + __log2f(lsum)) * kLn2;
-      a.D[(int64_t)bh * N + i] = dsum;
-    }
+  }
+  const float dsum = group_sum(dpart);
+  if (i < N && g == 0) {
+    a.L[(int64_t)bh * N + i] = (m + __log2f(lsum)) * kLn2;
+    a.D[(int64_t)bh * N + i] = dsum;
   }
 }
 
-template <typename T, int D, int NI>
+template <typename T, int D, int NW, int BC, bool TP2>
 hipError_t launch_t(const Problem& p, const FwdArgs& a, hipStream_t s) {
-  constexpr int kBR = 4 * 16 * NI;
+  constexpr int kBR = NW * 16;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
   const int total = n_row_tiles * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, NI, true>), dim3(total), dim3(kThreads), 0, s, a, p.Hq,
-                       group, p.N, p.tau, n_row_tiles, total);
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BC, TP2, true>), dim3(total), dim3(NW * 64), 0, s, a,
+                       p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, NI, false>), dim3(total), dim3(kThreads), 0, s, a, p.Hq,
-                       group, p.N, p.tau, n_row_tiles, total);
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BC, TP2, false>), dim3(total), dim3(NW * 64), 0, s, a,
+                       p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
 }
 
@@ -191,11 +180,14 @@ hipError_t launch_t(const Problem& p, const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
   if (p.bf16) {
-    if (p.d == 64) return launch_t<__bf16, 64, 2>(p, a, s);
-    return launch_t<__bf16, 128, 2>(p, a, s);
+    if (p.d == 64) {
+      if (tau_is_pow2(p.tau)) return launch_t<__bf16, 64, 8, 64, true>(p, a, s);
+      return launch_t<__bf16, 64, 8, 64, false>(p, a, s);
+    }
+    return launch_t<__bf16, 128, 8, 32, false>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 1>(p, a, s);
-  return launch_t<float, 128, 1>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 32, false>(p, a, s);
+  return launch_t<float, 128, 4, 32, false>(p, a, s);
 }
 
 }  // namespace fbob
