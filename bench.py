@@ -90,6 +90,63 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "extrapolated_full_step_s": dt * (w.N / rows_done) * w.B * w.H}
 
 
+def max_n_sweep(args):
+    """Sweep the sequence length of one long head (B=1 H=1 d=64 bf16, the
+    long-context workload's shape) upward by powers of two while the next call
+    is predicted (N^2 scaling) to stay under --max-seconds.  Each length runs the
+    forward and one timed BoB call, then checks size-independent properties of
+    the outputs: all finite, and the column sums of dK~ and dV~ vanish (Phi is
+    invariant under K -> K + 1c^T and V -> V + 1c^T)."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    dev = torch.device("cuda:0")
+    d = 64
+    tau = 1.0 / math.sqrt(d)
+    g = torch.Generator(device=dev)
+    results = []
+    n = args.max_n_start
+    free, total_mem = torch.cuda.mem_get_info()
+    # bytes per position: 7 bf16 inputs + O, dQ~, dK~, dV~, ddO~ (fp32) + L, D, alpha, E
+    per_pos = 7 * d * 2 + 5 * d * 4 + 4 * 4
+    while True:
+        g.manual_seed(1005 + n)
+        T = [torch.randn((1, 1, n, d), generator=g, device=dev).to(torch.bfloat16)
+             for _ in range(7)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        O, L, D = fb.forward(T[0], T[1], T[2], T[3], tau)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        out = fb.bob(*T, O, L, D, tau)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        ok = all(bool(torch.isfinite(v).all()) for v in out.values())
+        ratios = {}
+        for k in ("dKt", "dVt"):
+            x = out[k][0, 0].double()
+            ratios[k] = float((x.sum(0).abs() / x.abs().sum(0).clamp_min(1e-30)).max())
+        ok = ok and all(r < 1e-2 for r in ratios.values())
+        bob_s = t2 - t1
+        rec = {"N": n, "forward_s": round(t1 - t0, 4), "bob_s": round(bob_s, 4),
+               "bob_tflops": round(38.0 * n * n * d / bob_s / 1e12, 1),
+               "colsum_ratio": {k: float(f"{v:.2e}") for k, v in ratios.items()}, "ok": ok}
+        results.append(rec)
+        print(f"[max-n] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del T, O, L, D, out
+        torch.cuda.empty_cache()
+        if not ok or bob_s * 4 > args.max_seconds:
+            break
+        n *= 2
+    verified = max((r["N"] for r in results if r["ok"]), default=0)
+    line = {"metric": "max N on 1 GPU (exact BoB, B=1 H=1 d=64 bf16)", "value": verified,
+            "unit": "positions", "higher_is_better": True, "n_gpus": 1,
+            "sweep": results, "max_seconds_per_call": args.max_seconds,
+            "memory_bound_N": int(total_mem // per_pos),
+            "bytes_per_position": per_pos,
+            "data": "synthetic (torch.randn on device, seeded)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +154,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--max-n", action="store_true",
+                    help="sweep N for one long head instead of the headline step")
+    ap.add_argument("--max-n-start", type=int, default=1 << 18)
+    ap.add_argument("--max-seconds", type=float, default=20.0,
+                    help="stop before a BoB call predicted to exceed this many seconds")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (one head-parallel kernel set per "
@@ -107,6 +169,14 @@ def main():
     import torch
     import workloads
     import exact_softmax_attention_fbob_amd as fb
+
+    if args.max_n:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(3)
+        fb.load_library()
+        max_n_sweep(args)
+        return
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]

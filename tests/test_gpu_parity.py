@@ -162,3 +162,13 @@ def test_empty_problem_writes_nothing():
     out = fb.bob(z, z, z, z, z, z, z, O, L, D)
     torch.cuda.synchronize()
     assert all(v.numel() == 0 for v in out.values())
+
+
+def test_n1m_single_head_sampled_rows_and_invariants():
+    """N = 2^20 (four times the long-context workload), B=1 H=1 d=64 bf16."""
+    w = case("h1_n1048576_d64_bf16", 1, 1, 1 << 20, 64, "bf16", 1006)
+    U.say(f"[parity] {w.name}")
+    inp = U.make_inputs(w)
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    _check_sampled_rows(w, inp, gpu, n_rows=8)
+    _check_invariants(gpu)
