@@ -82,11 +82,13 @@ def cpu_baseline(w, budget_s: float = 12.0):
                              w.tau, rows, w.causal)
         rows_done += len(rows)
     dt = time.perf_counter() - t0
-    flops = 42.0 * rows_done * w.N * w.d  # same FLOP formula, for the sampled rows
+    # same FLOP formula, for the (i, j) pairs of the sampled rows
+    pairs = rows_done * (rows_done + 1) / 2.0 if w.causal else float(rows_done) * w.N
+    flops = 42.0 * pairs * w.d
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{rows_done} of {w.N} rows of head 0 of {w.B * w.H} heads "
-                      f"({rows_done * w.N * w.d * 42:.3e} FLOP, {dt:.1f} s, fp64 numpy)",
+                      f"({flops:.3e} FLOP, {dt:.1f} s, fp64 numpy)",
             "extrapolated_full_step_s": dt * (w.N / rows_done) * w.B * w.H}
 
 
@@ -186,6 +188,8 @@ def main():
     fb.load_library()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    torch.cuda.init()
+    torch.cuda.reset_peak_memory_stats(dev)
     print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w)
     T = {k: torch.from_numpy(v).to(dev).to(td).contiguous() for k, v in inp.items()}
@@ -248,7 +252,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     heads = B * H
-    n2d = float(N) * N * d * heads
+    # causal: only the (i, j) pairs with j <= i count, N (N + 1) / 2 of N^2
+    pairs = N * (N + 1) / 2.0 if causal else float(N) * N
+    n2d = pairs * d * heads
     f_fwd, f_p1, f_p2 = 4 * n2d, 22 * n2d, 16 * n2d
     peak = PEAK_TFLOPS[w.dtype]
     bob_tflops = (f_p1 + f_p2) / (bob_ms * 1e-3) / 1e12
@@ -276,7 +282,9 @@ def main():
         "bob_pct_bf16_peak": round(100 * bob_tflops / PEAK_TFLOPS["bf16"], 2),
         "kernels_ms": {"fwd_stats": round(float(fwd_ms), 4), "bob_pass1": round(float(p1_ms), 4),
                        "bob_pass2": round(float(p2_ms), 4)},
-        "flop_formula": "per (b,h): forward 4 N^2 d, pass1 22 N^2 d, pass2 16 N^2 d",
+        "flop_formula": "per (b,h): forward 4 N^2 d, pass1 22 N^2 d, pass2 16 N^2 d"
+                        + ("; causal counts N(N+1)/2 of the N^2 pairs" if causal else ""),
+        "peak_mem_mib": round(torch.cuda.max_memory_allocated(dev) / 2**20, 1),
         "roofline": {
             "kernel": "bob_pass1",
             "bound": "mfma",

@@ -56,7 +56,10 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bh = logical / n_row_tiles, rt = logical % n_row_tiles;
+  const int bh = logical / n_row_tiles;
+  // Causal rows near the end see the most keys: dispatch them first so the
+  // shortest tiles fill the tail of the grid.
+  const int rt = CAUSAL ? n_row_tiles - 1 - logical % n_row_tiles : logical % n_row_tiles;
   const int b = bh / Hq, h = bh % Hq, hk = h / group;
   const int64_t q_off = (int64_t)bh * N * D;
   const int64_t kv_off = ((int64_t)b * (Hq / group) + hk) * N * D;
