@@ -23,6 +23,8 @@ from .fbob_oracle import (  # noqa: F401
     attention_probs,
     forward,
     first_backward,
+    first_backward_rows,
+    first_backward_blocked,
     phi,
     bob,
     bob_affine,

@@ -116,6 +116,43 @@ def first_backward(Q, K, V, dO, tau, causal=False):
     return dQ, dK, dV
 
 
+def first_backward_rows(Q, K, V, dO, tau, rows, causal=False):
+    """dQ and D for the selected query rows only (same formulas as ``first_backward``).
+
+    Exact: row i of dQ needs only row i of Q and dO and all of K, V.
+    """
+    rows = np.asarray(rows)
+    Q, K, V, dO = map(_f64, (Q, K, V, dO))
+    P, _ = attention_probs(Q[rows], K, tau, causal, row_ids=rows)
+    dP = dO[rows] @ V.T
+    D = _rowsum(P * dP)
+    dS = P * (dP - _col(D))
+    return dict(dQ=tau * (dS @ K), D=D)
+
+
+def first_backward_blocked(Q, K, V, dO, tau, causal=False, row_block=1024):
+    """dQ, dK, dV, D of ``first_backward`` with rows taken ``row_block`` at a time.
+
+    Rows are independent; dK and dV are sums over rows, accumulated block by block.
+    Memory O(row_block N) instead of O(N^2).
+    """
+    Q, K, V, dO = map(_f64, (Q, K, V, dO))
+    N, d = Q.shape
+    dQ, D = np.empty((N, d)), np.empty(N)
+    dK, dV = np.zeros((N, d)), np.zeros((N, d))
+    for r0 in range(0, N, row_block):
+        rows = np.arange(r0, min(N, r0 + row_block))
+        P, _ = attention_probs(Q[rows], K, tau, causal, row_ids=rows)
+        dP = dO[rows] @ V.T
+        Dr = _rowsum(P * dP)
+        dS = P * (dP - _col(Dr))
+        dQ[rows] = tau * (dS @ K)
+        D[rows] = Dr
+        dK += tau * (dS.T @ Q[rows])
+        dV += P.T @ dO[rows]
+    return dict(dQ=dQ, dK=dK, dV=dV, D=D)
+
+
 def phi(Q, K, V, dO, UQ, UK, UV, tau, causal=False):
     """Phi = <dQ,U_Q> + <dK,U_K> + <dV,U_V> (FlashBoB notes, "整体框架")."""
     dQ, dK, dV = first_backward(Q, K, V, dO, tau, causal)

@@ -371,8 +371,39 @@ def test_fd_pin_catches_planted_mistakes(monkeypatch, mutation):
     assert worst > 1e-3, f"mutation {mutation} not detected (worst rel err {worst})"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_first_backward_rows_and_blocks_agree_with_plain(causal):
+    """The row-restricted and row-blocked first backward equal the plain one, whose
+    own pins are the finite differences and torch autograd above."""
+    N, d = 75, 8
+    t = rand_inputs(N, d, seed=93)
+    tau = 1 / math.sqrt(d)
+    dQ, dK, dV = fo.first_backward(t["Q"], t["K"], t["V"], t["dO"], tau, causal)
+    _, _, D = fo.forward(t["Q"], t["K"], t["V"], t["dO"], tau, causal)
+    blk = fo.first_backward_blocked(t["Q"], t["K"], t["V"], t["dO"], tau, causal, row_block=16)
+    for k, ref in (("dQ", dQ), ("dK", dK), ("dV", dV), ("D", D)):
+        assert rel_err(blk[k], ref) < 1e-13, k
+    rows = np.array([0, 8, 40, 74])
+    r = fo.first_backward_rows(t["Q"], t["K"], t["V"], t["dO"], tau, rows, causal)
+    assert rel_err(r["dQ"], dQ[rows]) < 1e-13
+    assert rel_err(r["D"], D[rows]) < 1e-12
+
+
+def test_first_backward_column_sums():
+    """Exact identities of the first backward at any size: sum_j dK_j = 0 (rows of
+    dS sum to zero) and sum_j dV_j = sum_i dO_i (rows of P sum to one)."""
+    N, d = 40, 6
+    t = rand_inputs(N, d, seed=94)
+    for causal in (False, True):
+        out = fo.first_backward_blocked(t["Q"], t["K"], t["V"], t["dO"], 0.4, causal, row_block=7)
+        assert np.max(np.abs(out["dK"].sum(axis=0))) < 1e-12 * np.abs(out["dK"]).sum()
+        np.testing.assert_allclose(out["dV"].sum(axis=0), t["dO"].sum(axis=0), rtol=1e-12,
+                                   atol=1e-12)
+
+
 def test_oracle_package_exports():
-    for name in ("forward", "first_backward", "phi", "bob", "bob_affine", "bob_rows",
+    for name in ("forward", "first_backward", "first_backward_rows", "first_backward_blocked",
+                 "phi", "bob", "bob_affine", "bob_rows",
                  "bob_blocked", "bob_columns", "attention_probs"):
         assert callable(getattr(oracle, name))
 
