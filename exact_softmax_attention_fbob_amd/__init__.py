@@ -8,12 +8,14 @@ torch's current HIP stream to the library.  Every step of the computation runs
 in the library's HIP kernels; there is no fallback path.
 
 Entry points (same names as the C ABI):
-    forward(Q, K, V, dO, tau, causal)              -> O, L, D
+    forward(Q, K, V, dO, tau, causal)              -> O, L, D   (dO=None: O, L, None)
+    backward(Q, K, V, dO, O, L, tau, causal)       -> dict(dQ, dK, dV, D)
     bob(Q, K, V, dO, UQ, UK, UV, O, L, D, ...)     -> dict(dQt, dKt, dVt, ddOt, alpha, E)
     bob_pass1(...)                                  -> dict(dQt, ddOt, alpha, E)
     bob_pass2(..., alpha, E)                        -> dict(dKt, dVt)
 Shapes: Q, dO, U_Q: [B, Hq, N, d]; K, V, U_K, U_V: [B, Hkv, N, d]; L, D, alpha,
-E: [B, Hq, N]; all outputs float32.
+E: [B, Hq, N]; all outputs float32.  ``autograd.attention`` wraps forward,
+backward and bob as a twice-differentiable torch operation.
 """
 
 from __future__ import annotations
@@ -24,7 +26,7 @@ import os
 
 from ._lib import FbobError, load_library, STATUS  # noqa: F401
 
-__all__ = ["forward", "bob", "bob_pass1", "bob_pass2", "load_library", "FbobError",
+__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "load_library", "FbobError",
            "library_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,17 +102,44 @@ def _tau(tau, d):
     return ctypes.c_float(1.0 / math.sqrt(d) if tau is None else float(tau))
 
 
-def forward(Q, K, V, dO, tau=None, causal=False):
-    """O, L, D for the BoB row state (C ABI ``fbob_forward``)."""
+def forward(Q, K, V, dO=None, tau=None, causal=False):
+    """O, L, D for the BoB row state (C ABI ``fbob_forward``).
+
+    With ``dO=None`` only the attention forward runs and D is returned as None.
+    """
     torch = _torch()
     lib = load_library()
     B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO)
     O = torch.empty((B, Hq, N, d), dtype=torch.float32, device=Q.device)
     L = torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
-    D = torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
+    D = None if dO is None else torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
     _call(lib.fbob_forward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
-          _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L), _p(D), _stream())
+          _p(Q), _p(K), _p(V), None if dO is None else _p(dO), _p(O), _p(L),
+          None if D is None else _p(D), _stream())
     return O, L, D
+
+
+def backward(Q, K, V, dO, O, L, tau=None, causal=False):
+    """First-order gradients dQ, dK, dV and the row scalar D (C ABI ``fbob_backward``).
+
+    O and L come from ``forward`` on the same (Q, K, V); the returned D completes
+    the row state (O, L, D) that ``bob`` takes.  dK and dV have the key/value heads'
+    shape (grouped query heads are summed).
+    """
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO)
+    _check_f32(O, (B, Hq, N, d), "O")
+    _check_f32(L, (B, Hq, N), "L")
+    dev = Q.device
+    out = dict(dQ=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               dK=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               dV=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               D=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    _call(lib.fbob_backward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+          _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L),
+          _p(out["dQ"]), _p(out["dK"]), _p(out["dV"]), _p(out["D"]), _stream())
+    return out
 
 
 def _row_state(O, L, D, B, Hq, N, d):

@@ -20,6 +20,7 @@ _i64, _f, _i, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_
 _SIZES = [_i, _i64, _i64, _i64, _i64, _i64, _f, _i]  # dtype, B, Hq, Hkv, N, d, tau, causal
 PROTOTYPES = {
     "fbob_forward": (_i, _SIZES + [_vp] * 4 + [_vp] * 3 + [_vp]),
+    "fbob_backward": (_i, _SIZES + [_vp] * 4 + [_vp] * 2 + [_vp] * 4 + [_vp]),
     "fbob_bob": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp]),
     "fbob_bob_pass1": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 4 + [_vp]),
     "fbob_bob_pass2": (_i, _SIZES + [_vp] * 7 + [_vp] * 4 + [_vp] * 2 + [_vp]),

@@ -106,11 +106,14 @@ int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64
   const int64_t es = c.p.bf16 ? 2 : 4;
   const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
   const int64_t ob = B * Hq * N * d * 4, rb = B * Hq * N * 4;
+  // dO and D are both given (backward row state) or both NULL (forward only).
+  if ((dO == nullptr) != (D == nullptr)) return FBOB_ERR_INVALID_ARG;
+  const bool with_d = dO != nullptr;
   const void* ins[] = {Q, K, V, dO};
   const int64_t inb[] = {qb, kb, kb, qb};
   void* outs[] = {O, L, D};
   const int64_t outb[] = {ob, rb, rb};
-  const int st = check_ptrs(ins, inb, 4, outs, outb, 3);
+  const int st = check_ptrs(ins, inb, with_d ? 4 : 3, outs, outb, with_d ? 3 : 2);
   if (st != FBOB_OK) return st;
   fbob::FwdArgs a{Q, K, V, dO, O, L, D};
   return finish(fbob::launch_forward(c.p, a, static_cast<hipStream_t>(stream)));
@@ -154,6 +157,28 @@ int fbob_bob_pass2(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
   if (st != FBOB_OK) return st;
   fbob::Pass2Args a{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
   return finish(fbob::launch_pass2(c.p, a, static_cast<hipStream_t>(stream)));
+}
+
+int fbob_backward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+                  int causal, const void* Q, const void* K, const void* V, const void* dO,
+                  const float* O, const float* L, float* dQ, float* dK, float* dV, float* D,
+                  void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (c.empty) return FBOB_OK;
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO, O, L};
+  const int64_t inb[] = {qb, kb, kb, qb, ob, rb};
+  void* outs[] = {dQ, dK, dV, D};
+  const int64_t outb[] = {ob, kob, kob, rb};
+  const int st = check_ptrs(ins, inb, 6, outs, outb, 4);
+  if (st != FBOB_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  fbob::GradArgs a{Q, K, V, dO, O, L, dQ, dK, dV, D};
+  if (fbob::launch_grad_dq(c.p, a, s) != hipSuccess) return FBOB_ERR_HIP;
+  return finish(fbob::launch_grad_dkv(c.p, a, s));
 }
 
 int fbob_bob(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,

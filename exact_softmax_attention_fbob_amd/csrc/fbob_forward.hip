@@ -47,7 +47,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
   const int64_t q_off = (int64_t)bh * N * D;
   const int64_t kv_off = ((int64_t)b * (Hq / group) + hk) * N * D;
   const T* Qh = reinterpret_cast<const T*>(a.Q) + q_off;
-  const T* dOh = reinterpret_cast<const T*>(a.dO) + q_off;
   const T* const kv_bases[2] = {reinterpret_cast<const T*>(a.K) + kv_off,
                                 reinterpret_cast<const T*>(a.V) + kv_off};
 
@@ -143,9 +142,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
     if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
   }
 
-  // Epilogue: O = acc / l, L = (m + log2 l) ln 2, D = dO . O (fp32 O).
+  // Epilogue: O = acc / l, L = (m + log2 l) ln 2, and D = dO . O (fp32 O) when
+  // dO is given (a uniform branch).
   const float lsum = accL[0];
   const float inv = 1.f / lsum;
+  const bool with_d = a.dO != nullptr;
   float dpart = 0.f;
   if (i < N) {
 #pragma unroll
@@ -153,14 +154,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
       const int d0 = 16 * db + 4 * g;
       const f32x4 o = acc[db] * inv;
       *reinterpret_cast<f32x4*>(a.O + q_off + (int64_t)i * D + d0) = o;
+      if (with_d) {
+        const T* dOh = reinterpret_cast<const T*>(a.dO) + q_off;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dpart += (float)dOh[(int64_t)i * D + d0 + q] * o[q];
+        for (int q = 0; q < 4; ++q) dpart += (float)dOh[(int64_t)i * D + d0 + q] * o[q];
+      }
     }
   }
   const float dsum = group_sum(dpart);
   if (i < N && g == 0) {
     a.L[(int64_t)bh * N + i] = (m + __log2f(lsum)) * kLn2;
-    a.D[(int64_t)bh * N + i] = dsum;
+    if (with_d) a.D[(int64_t)bh * N + i] = dsum;
   }
 }
 

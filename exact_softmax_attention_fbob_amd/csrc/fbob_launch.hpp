@@ -16,7 +16,7 @@ struct Problem {
 };
 
 struct FwdArgs {
-  const void *Q, *K, *V, *dO;
+  const void *Q, *K, *V, *dO;  // dO may be NULL: then D is not written
   float *O, *L, *D;
 };
 
@@ -32,8 +32,17 @@ struct Pass2Args {
   float *dKt, *dVt;
 };
 
+// First-order backward: the row pass writes dQ and D, the column pass reads D.
+struct GradArgs {
+  const void *Q, *K, *V, *dO;
+  const float *O, *L;
+  float *dQ, *dK, *dV, *D;
+};
+
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s);
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s);
+hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s);
+hipError_t launch_grad_dkv(const Problem& p, const GradArgs& a, hipStream_t s);
 
 }  // namespace fbob

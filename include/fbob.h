@@ -74,11 +74,34 @@ typedef enum { FBOB_DTYPE_F32 = 0, FBOB_DTYPE_BF16 = 1 } fbob_dtype;
  *   out: O [B,Hq,N,d] = P V (fp32)
  *        L [B,Hq,N]   = log sum_j exp(tau Q_i . K_j)     (fp32, natural log)
  *        D [B,Hq,N]   = dO_i . O_i                        (fp32, from fp32 O)
+ * dO and D may both be NULL: then only O and L are computed (the attention
+ * forward alone); exactly one of them NULL is FBOB_ERR_INVALID_ARG.
  */
 int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                  float tau, int causal,
                  const void* Q, const void* K, const void* V, const void* dO,
                  float* O, float* L, float* D, void* stream);
+
+/*
+ * First-order attention backward (FlashAttention blog, "FlashAttention 的反向传播
+ * 设计", section 一 for dV = P^T dO, dS = P o (dP - D), dQ = tau dS K,
+ * dK = tau dS^T Q, and section 二 for rebuilding P on chip from L).  Two passes
+ * like the BoB (FlashBoB notes, "关键设计" 2): a row pass writes dQ and D, then a
+ * column pass writes dK and dV (query heads of a group summed on chip); every
+ * output is written once, no atomics.
+ *
+ *   in : Q, dO [B,Hq,N,d], K, V [B,Hkv,N,d] (dtype);
+ *        O [B,Hq,N,d], L [B,Hq,N] (fp32) from fbob_forward on the same
+ *        (Q, K, V, tau, causal); anything else gives undefined (but
+ *        memory-safe) results.
+ *   out: dQ [B,Hq,N,d]; dK, dV [B,Hkv,N,d]; D [B,Hq,N] = dO_i . O_i  (fp32).
+ *        (O, L, D) is then the complete row state that fbob_bob takes.
+ */
+int fbob_backward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                  float tau, int causal,
+                  const void* Q, const void* K, const void* V, const void* dO,
+                  const float* O, const float* L,
+                  float* dQ, float* dK, float* dV, float* D, void* stream);
 
 /*
  * Exact BoB: Pass 1 then Pass 2 on the same stream (FlashBoB notes,

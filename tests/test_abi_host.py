@@ -35,8 +35,8 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
-        ["fbob_forward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2", "fbob_strerror",
-         "fbob_version"])
+        ["fbob_forward", "fbob_backward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
+         "fbob_strerror", "fbob_version"])
     assert sorted(_lib.PROTOTYPES) == declared_functions()
 
 
@@ -126,6 +126,54 @@ def test_pass_entry_points_validate_too(lib):
     q = list(p[:13])
     q[12] = ctypes.c_void_p(fb.addrs[0])  # dVt aliases Q
     assert lib.fbob_bob_pass2(1, 1, 2, 2, 64, 64, ctypes.c_float(0.1), 0, *q, s) == ALIAS
+
+
+def call_backward(lib, dtype=1, B=1, Hq=2, Hkv=2, N=64, d=64, tau=0.125, causal=0, ptrs=None):
+    p = ptrs or [FakeBuffers(10)[k] for k in range(10)]
+    return lib.fbob_backward(dtype, B, Hq, Hkv, N, d, ctypes.c_float(tau), causal, *p[:10],
+                             ctypes.c_void_p(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(dtype=3), INVALID), (dict(Hq=4, Hkv=3), INVALID),
+    (dict(tau=float("inf")), INVALID), (dict(N=0), OK), (dict(B=0), OK),
+])
+def test_backward_size_validation(lib, kw, status):
+    assert call_backward(lib, **kw) == status
+
+
+def test_backward_pointer_validation(lib):
+    fb = FakeBuffers(10)
+    for k in range(10):
+        ptrs = [fb[m] for m in range(10)]
+        ptrs[k] = ctypes.c_void_p(0)
+        assert call_backward(lib, ptrs=ptrs) == INVALID, k
+        ptrs[k] = ctypes.c_void_p(fb.addrs[k] + 4)
+        assert call_backward(lib, ptrs=ptrs) == ALIGN, k
+    # D (index 9) inside L (index 5); dQ (6) overlapping dK (7)
+    ptrs = [fb[m] for m in range(10)]
+    ptrs[9] = ctypes.c_void_p(fb.addrs[5] + 64)
+    assert call_backward(lib, ptrs=ptrs) == ALIAS
+    ptrs = [fb[m] for m in range(10)]
+    ptrs[7] = ctypes.c_void_p(fb.addrs[6] + 1024)
+    assert call_backward(lib, ptrs=ptrs) == ALIAS
+
+
+def test_forward_without_do_needs_both_null(lib):
+    fb = FakeBuffers(7)
+    p = [fb[m] for m in range(7)]
+    # dO (3) NULL with D (6) given, and the reverse: invalid
+    q = list(p)
+    q[3] = ctypes.c_void_p(0)
+    assert call_forward(lib, ptrs=q) == INVALID
+    q = list(p)
+    q[6] = ctypes.c_void_p(0)
+    assert call_forward(lib, ptrs=q) == INVALID
+    # both NULL passes the NULL check: a misaligned Q is then what is reported
+    q = list(p)
+    q[3] = q[6] = ctypes.c_void_p(0)
+    q[0] = ctypes.c_void_p(fb.addrs[0] + 2)
+    assert call_forward(lib, ptrs=q) == ALIGN
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path):
