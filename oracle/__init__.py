@@ -28,6 +28,7 @@ from .fbob_oracle import (  # noqa: F401
     phi,
     bob,
     bob_affine,
+    hvp_half_squared_output,
     bob_rows,
     bob_row_block,
     bob_blocked,

@@ -208,6 +208,21 @@ def bob(Q, K, V, dO, UQ, UK, UV, tau, causal=False):
                 alpha=r["alpha"], E=r["E"])
 
 
+def hvp_half_squared_output(Q, K, V, UQ, UK, UV, tau, causal=False):
+    """Hessian-vector product of loss = 0.5 ||O||^2 in the direction (U_Q, U_K, U_V).
+
+    The use the FlashBoB notes give for BoB (Sophia-H curvature estimates: the
+    gradient of <grad loss, u>).  Here the upstream gradient dO = O depends on
+    (Q, K, V) as well, so the product is the BoB at dO = O plus the first backward
+    applied to the BoB's ddO~ (the path through dO).
+    """
+    Q, K, V, UQ, UK, UV = map(_f64, (Q, K, V, UQ, UK, UV))
+    O, _, _ = forward(Q, K, V, np.zeros_like(Q), tau, causal)
+    b = bob(Q, K, V, O, UQ, UK, UV, tau, causal)
+    dQ2, dK2, dV2 = first_backward(Q, K, V, b["ddOt"], tau, causal)
+    return dict(dQ=b["dQt"] + dQ2, dK=b["dKt"] + dK2, dV=b["dVt"] + dV2)
+
+
 def bob_affine(Q, K, V, dO, UQ, UK, UV, tau, causal=False):
     """Row outputs through the hierarchical affine decomposition.
 

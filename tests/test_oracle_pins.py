@@ -389,6 +389,26 @@ def test_first_backward_rows_and_blocks_agree_with_plain(causal):
     assert rel_err(r["D"], D[rows]) < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_hvp_of_squared_output_matches_fd_of_gradient(causal):
+    """The HVP composition against a central difference of the first-order gradient
+    of 0.5 ||O||^2 (first backward at dO = O) along the direction U."""
+    N, d = 9, 4
+    t = rand_inputs(N, d, seed=95)
+    tau = 0.6
+    h = 1e-5
+
+    def grad_at(s):
+        Q, K, V = t["Q"] + s * t["UQ"], t["K"] + s * t["UK"], t["V"] + s * t["UV"]
+        O, _, _ = fo.forward(Q, K, V, np.zeros_like(Q), tau, causal)
+        return fo.first_backward(Q, K, V, O, tau, causal)
+
+    gp, gm = grad_at(h), grad_at(-h)
+    hv = fo.hvp_half_squared_output(*args(t)[:3], t["UQ"], t["UK"], t["UV"], tau, causal)
+    for k, a, b in zip(("dQ", "dK", "dV"), gp, gm):
+        assert rel_err(hv[k], (a - b) / (2 * h)) < 1e-7, k
+
+
 def test_first_backward_column_sums():
     """Exact identities of the first backward at any size: sum_j dK_j = 0 (rows of
     dS sum to zero) and sum_j dV_j = sum_i dO_i (rows of P sum to one)."""
@@ -403,7 +423,7 @@ def test_first_backward_column_sums():
 
 def test_oracle_package_exports():
     for name in ("forward", "first_backward", "first_backward_rows", "first_backward_blocked",
-                 "phi", "bob", "bob_affine", "bob_rows",
+                 "phi", "bob", "bob_affine", "bob_rows", "hvp_half_squared_output",
                  "bob_blocked", "bob_columns", "attention_probs"):
         assert callable(getattr(oracle, name))
 
