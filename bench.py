@@ -9,8 +9,15 @@ launches, issued as fbob_bob_pass1 + fbob_bob_pass2 so that each kernel can be
 bracketed by HIP events on the stream it runs on).  Inputs are resident in HBM
 before the timed region starts.
 
-FLOP formula (per (batch, head), non-causal, fixed): forward 4 N^2 d,
-Pass 1 22 N^2 d, Pass 2 16 N^2 d; BoB = 38 N^2 d; step = 42 N^2 d.
+FLOP formula (per (batch, query head), non-causal, fixed): forward 4 N^2 d,
+Pass 1 22 N^2 d, Pass 2 16 N^2 d; BoB = 38 N^2 d; step = 42 N^2 d.  Causal
+workloads count the N (N + 1) / 2 unmasked (i, j) pairs instead of N^2.
+
+After the timed step, two related operations are timed on the same inputs
+(reported under "extras", outside `value`): the first-order backward
+(fbob_backward, algorithmic 10 N^2 d: the five products of the backward) and one
+Hessian-vector step through the autograd layer (forward, first backward with
+create_graph, then the BoB as the backward of the backward).
 
 Prints ONE JSON line.  `value` is the step's TFLOP/s; the BoB-only ms/call and
 TFLOP/s (the headline) are reported alongside, with the dominant kernel's
@@ -92,6 +99,70 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "extrapolated_full_step_s": dt * (w.N / rows_done) * w.B * w.H}
 
 
+def time_extras(fb, lib, T, O, L, w, Hkv, n2d, bob_ms, fwd_ms, stream, steps):
+    """Time fbob_backward (HIP events on `stream`) and one autograd Hessian-vector
+    step on the bench inputs; O, L come from the timed forward."""
+    import ctypes
+    import torch
+    from exact_softmax_attention_fbob_amd.autograd import attention
+    B, H, N, d, tau, causal = w.B, w.H, w.N, w.d, w.tau, w.causal
+    dev = O.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dQ=torch.empty((B, H, N, d), **f32), dK=torch.empty((B, Hkv, N, d), **f32),
+             dV=torch.empty((B, Hkv, N, d), **f32), D=torch.empty((B, H, N), **f32))
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    dt_code = 1 if w.dtype == "bf16" else 0
+
+    def bwd():
+        st = lib.fbob_backward(dt_code, B, H, Hkv, N, d, ctypes.c_float(tau), int(causal),
+                               p(T["Q"]), p(T["K"]), p(T["V"]), p(T["dO"]), p(O), p(L),
+                               p(g["dQ"]), p(g["dK"]), p(g["dV"]), p(g["D"]), sp)
+        if st != 0:
+            raise fb.FbobError(st)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    bwd_ms = timed(bwd, steps)
+    Q, K, V, dO = (T[k].clone().requires_grad_(True) for k in ("Q", "K", "V", "dO"))
+    U = [T[k].float() for k in ("UQ", "UK", "UV")]
+
+    def hvp():
+        o = attention(Q, K, V, tau, causal)
+        gr = torch.autograd.grad(o, (Q, K, V), grad_outputs=dO, create_graph=True)
+        phi = sum((gi.float() * u).sum() for gi, u in zip(gr, U))
+        torch.autograd.grad(phi, (Q, K, V, dO))
+
+    hvp_ms = timed(hvp, max(2, steps // 4))
+    peak = PEAK_TFLOPS[w.dtype]
+    alg = 10 * n2d / (bwd_ms * 1e-3) / 1e12
+    return {
+        "first_backward": {
+            "ms_per_call": round(bwd_ms, 4),
+            "tflops_algorithmic": round(alg, 2),
+            "pct_peak": round(100 * alg / peak, 2),
+            "tflops_executed": round(14 * n2d / (bwd_ms * 1e-3) / 1e12, 2),
+            "flop_formula": "algorithmic 10 N^2 d (S, dP, dV, dQ, dK); executed 14 N^2 d "
+                            "(row pass S, dP, dQ; column pass S, dP, dK, dV)",
+        },
+        "autograd_hvp_step": {
+            "ms": round(hvp_ms, 4),
+            "kernels_only_ms": round(float(fwd_ms) + bwd_ms + float(bob_ms), 4),
+            "what": "attention(Q,K,V) forward, grad with create_graph, grad of "
+                    "<dQ,U_Q>+<dK,U_K>+<dV,U_V> w.r.t. (Q,K,V,dO)",
+        },
+    }
+
+
 def max_n_sweep(args):
     """Sweep the sequence length of one long head (B=1 H=1 d=64 bf16, the
     long-context workload's shape) upward by powers of two while the next call
@@ -156,6 +227,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip timing the first-order backward and the autograd HVP step")
     ap.add_argument("--max-n", action="store_true",
                     help="sweep N for one long head instead of the headline step")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
@@ -195,6 +268,10 @@ def main():
     T = {k: torch.from_numpy(v).to(dev).to(td).contiguous() for k, v in inp.items()}
     del inp
     B, H, N, d, tau, causal = w.B, w.H, w.N, w.d, w.tau, w.causal
+    Hkv = int(w.extra.get("Hkv", H))  # grouped-query workloads keep the first Hkv heads
+    if Hkv != H:
+        for k in ("K", "V", "UK", "UV"):
+            T[k] = T[k][:, :Hkv].contiguous()
     f32 = dict(dtype=torch.float32, device=dev)
     O = torch.empty((B, H, N, d), **f32)
     L = torch.empty((B, H, N), **f32)
@@ -204,7 +281,8 @@ def main():
     lib = fb.load_library()
     import ctypes
     p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    out = {k: torch.empty((B, H, N, d), **f32) for k in ("dQt", "dKt", "dVt", "ddOt")}
+    out = {k: torch.empty((B, H if k in ("dQt", "ddOt") else Hkv, N, d), **f32)
+           for k in ("dQt", "dKt", "dVt", "ddOt")}
     out.update(alpha=torch.empty((B, H, N), **f32), E=torch.empty((B, H, N), **f32))
     dt_code = 1 if w.dtype == "bf16" else 0
     ctau = ctypes.c_float(tau)
@@ -218,16 +296,16 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        check(lib.fbob_forward(dt_code, B, H, H, N, d, ctau, int(causal), *map(p, qargs[:4]),
+        check(lib.fbob_forward(dt_code, B, H, Hkv, N, d, ctau, int(causal), *map(p, qargs[:4]),
                                p(O), p(L), p(D), sp))
         if ev is not None:
             ev[1].record(stream)
-        check(lib.fbob_bob_pass1(dt_code, B, H, H, N, d, ctau, int(causal), *map(p, qargs),
+        check(lib.fbob_bob_pass1(dt_code, B, H, Hkv, N, d, ctau, int(causal), *map(p, qargs),
                                  p(O), p(L), p(D), p(out["dQt"]), p(out["ddOt"]),
                                  p(out["alpha"]), p(out["E"]), sp))
         if ev is not None:
             ev[2].record(stream)
-        check(lib.fbob_bob_pass2(dt_code, B, H, H, N, d, ctau, int(causal), *map(p, qargs),
+        check(lib.fbob_bob_pass2(dt_code, B, H, Hkv, N, d, ctau, int(causal), *map(p, qargs),
                                  p(L), p(D), p(out["alpha"]), p(out["E"]),
                                  p(out["dKt"]), p(out["dVt"]), sp))
         if ev is not None:
@@ -251,6 +329,7 @@ def main():
     bob_ms = np.mean([e[1].elapsed_time(e[3]) for e in evs])
     ms_step = wall * 1e3 / args.steps
 
+    peak_mib = round(torch.cuda.max_memory_allocated(dev) / 2**20, 1)  # the step's own peak
     heads = B * H
     # causal: only the (i, j) pairs with j <= i count, N (N + 1) / 2 of N^2
     pairs = N * (N + 1) / 2.0 if causal else float(N) * N
@@ -274,7 +353,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+        "config": {"workload": name, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
                    "tau": tau, "inputs": "i.i.d. N(0,1), PCG64 seed %d" % w.seed,
                    "scale_u": w.scale_u, "scale_qk": w.scale_qk},
         "bob_ms_per_call": round(float(bob_ms), 4),
@@ -284,7 +363,7 @@ def main():
                        "bob_pass2": round(float(p2_ms), 4)},
         "flop_formula": "per (b,h): forward 4 N^2 d, pass1 22 N^2 d, pass2 16 N^2 d"
                         + ("; causal counts N(N+1)/2 of the N^2 pairs" if causal else ""),
-        "peak_mem_mib": round(torch.cuda.max_memory_allocated(dev) / 2**20, 1),
+        "peak_mem_mib": peak_mib,
         "roofline": {
             "kernel": "bob_pass1",
             "bound": "mfma",
@@ -295,6 +374,11 @@ def main():
             "traffic": measured_traffic(name),
         },
     }
+    if not args.no_extras:
+        print("[bench] extras: first-order backward, autograd HVP step", file=sys.stderr,
+              flush=True)
+        line["extras"] = time_extras(fb, lib, T, O, L, w, Hkv, n2d, bob_ms, fwd_ms, stream,
+                                     args.steps)
     if not args.no_cpu:
         print("[bench] cpu baseline (fp64 oracle, bounded sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)

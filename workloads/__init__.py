@@ -73,6 +73,12 @@ for _n, _d, _seed in ((4096, 64, 2001), (8192, 64, 2002), (16384, 64, 2003),
     WORKLOADS[_name] = Workload(_name, B=4, H=12, N=_n, d=_d, dtype="bf16", seed=_seed,
                                 causal=True, note="pages' benchmark shape (causal, B=4, H=12)")
 
+# Grouped-query attention at the headline size (FlashBoB notes, "关键设计" 3): 12 query
+# heads share 4 key/value heads (K, V, U_K, U_V keep heads 0..3 of the draw).
+WORKLOADS["gqa_h12_hkv4_n16384_d64_bf16"] = Workload(
+    "gqa_h12_hkv4_n16384_d64_bf16", B=1, H=12, N=16384, d=64, dtype="bf16", seed=2101,
+    note="grouped-query attention, group of 3", extra={"Hkv": 4})
+
 HEADLINE = "h12_n16384_d64_bf16_u01"
 
 
