@@ -306,6 +306,12 @@ struct MultiStager {
 // chunk p ^ swz(row).  No VGPRs hold the data and no ds_write is issued; the
 // caller waits on vmcnt before the barrier that publishes the tile.  Rows past
 // the end are clamped to the last row (finite data, given zero weight).
+//
+// Per lane only one 32-bit offset per instruction is kept (row within the 1 KiB
+// block times the row pitch plus the swizzled chunk); tensor bases, block rows
+// and LDS offsets are wave-uniform.  A stage that lies wholly inside the tensor
+// is addressed as uniform base + lane offset; only a stage that crosses the end
+// takes the per-lane clamp.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int ROWS, int NT, int NW>
 struct DirectStager {
@@ -318,34 +324,48 @@ struct DirectStager {
   static_assert(kInst % NW == 0, "staging instructions must divide evenly over waves");
   static constexpr int kPer = kInst / NW;  // instructions per wave
   static constexpr int kTileBytes = ROWS * kRB;
-  const char* src[kPer];  // tensor base + logical chunk column (per lane)
-  int row[kPer];          // tile row of this lane
-  int lds_off[kPer];      // wave-uniform LDS offset of the 1 KiB block
+  const char* base[kPer];  // tensor base of instruction k (wave-uniform)
+  int row_blk[kPer];       // first tile row of instruction k's block (wave-uniform)
+  int lds_off[kPer];       // LDS offset of instruction k's 1 KiB block (wave-uniform)
+  uint32_t voff[kPer];     // per lane: lrow * kRB + 16 * (swizzled chunk)
+  int lrow;                // per lane: row within the block
 
   // w must be wave-uniform.
   __device__ __forceinline__ void init(const T* const (&bases)[NT], int w, int lane) {
+    lrow = lane / kChunks;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int ii = k * NW + w;
       const int tensor = ii / kInstPerTensor, rg = ii % kInstPerTensor;
-      row[k] = rg * kRowsPerInst + lane / kChunks;
-      const int c = (lane % kChunks) ^ Tile<T, D>::swz(row[k]);
-      const T* base = bases[0];
+      row_blk[k] = rg * kRowsPerInst;
+      const int c = (lane % kChunks) ^ Tile<T, D>::swz(row_blk[k] + lrow);
+      voff[k] = (uint32_t)(lrow * kRB + c * 16);
+      const T* b = bases[0];
 #pragma unroll
       for (int m = 1; m < NT; ++m)
-        if (tensor == m) base = bases[m];
-      src[k] = reinterpret_cast<const char*>(base) + c * 16;
+        if (tensor == m) b = bases[m];
+      base[k] = reinterpret_cast<const char*>(b);
       lds_off[k] = tensor * kTileBytes + rg * 1024;
     }
   }
   __device__ __forceinline__ void load(char* tiles, int row0, int nrows, int64_t byte_off = 0) const {
     typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(1))) void glb_void;
+    if (row0 + ROWS <= nrows) {  // wave-uniform: the whole stage lies inside the tensor
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int gr = min(row0 + row[k], nrows - 1);
-      const char* gp = src[k] + byte_off + (int64_t)gr * kRB;
-      __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)(tiles + lds_off[k]), 16, 0, 0);
+      for (int k = 0; k < kPer; ++k) {
+        const char* gp = base[k] + byte_off + (int64_t)(row0 + row_blk[k]) * kRB + voff[k];
+        __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)(tiles + lds_off[k]), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        // rows past the end read the last row: shift this lane's row back
+        const int rb = row0 + row_blk[k];
+        const int shift = max(rb + lrow - (nrows - 1), 0);
+        const char* gp = base[k] + byte_off + ((int64_t)rb - shift) * kRB + voff[k];
+        __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)(tiles + lds_off[k]), 16, 0, 0);
+      }
     }
   }
 };
@@ -360,28 +380,52 @@ __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0
 // tile base plus a compile-time constant plus one of these registers.
 //   row(tile, rb, dc): A/B operand rows 16 rb + r, columns 32 dc + 8 g .. +7
 //   tr(tile, db):      transposed operand, lane (r, g) gets X[k(g, e)][16 db + r]
+// With XOR set (bf16 only) the lane keeps a single offset per pattern: the chunk
+// index enters the swizzle by XOR on bits that no other part of the offset uses,
+// so the offset of column block dc (db) is the dc = 0 (db = 0) offset XOR
+// dc << 6 (db << 5).  `fresh()` returns a copy whose offsets the compiler cannot
+// treat as loop invariants, so the XORs are formed once per use site inside the
+// loop instead of being hoisted into a table of registers.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool XOR = false>
 struct LdsLane {
   static constexpr int kRB = Tile<T, D>::kRowBytes;
   static constexpr int kDC = D / 32, kDB = D / 16;
-  int ro[kDC];
-  int to[kDB];
+  static constexpr bool kXor = XOR && sizeof(T) == 2;
+  int ro[kXor ? 1 : kDC];
+  int to[kXor ? 1 : kDB];
   int r, g;
 
   __device__ __forceinline__ LdsLane(int r_, int g_) : r(r_), g(g_) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int dc = 0; dc < kDC; ++dc) ro[dc] = Tile<T, D>::chunk_off(r, 4 * dc + g);
+      for (int dc = 0; dc < (kXor ? 1 : kDC); ++dc) ro[dc] = Tile<T, D>::chunk_off(r, 4 * dc + g);
       const int b = r >> 2, c = r & 3;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) to[db] = Tile<T, D>::elem_off(4 * g + b, 16 * db + 4 * c);
+      for (int db = 0; db < (kXor ? 1 : kDB); ++db)
+        to[db] = Tile<T, D>::elem_off(4 * g + b, 16 * db + 4 * c);
     }
+  }
+  __device__ __forceinline__ LdsLane fresh() const {
+    LdsLane o = *this;
+    if constexpr (kXor) {
+      asm volatile("" : "+v"(o.ro[0]));
+      asm volatile("" : "+v"(o.to[0]));
+    }
+    return o;
+  }
+  __device__ __forceinline__ int row_off(int dc) const {
+    if constexpr (kXor) return ro[0] ^ (dc << 6);
+    else return ro[dc];
+  }
+  __device__ __forceinline__ int tr_off(int db) const {
+    if constexpr (kXor) return to[0] ^ (db << 5);
+    else return to[db];
   }
   __device__ __forceinline__ typename Elem<T>::frag row(const char* tile, int rb, int dc) const {
     using F = typename Elem<T>::frag;
     if constexpr (sizeof(T) == 2) {
-      return *reinterpret_cast<const F*>(tile + rb * 16 * kRB + ro[dc]);
+      return *reinterpret_cast<const F*>(tile + rb * 16 * kRB + row_off(dc));
     } else {
       return lds_frag_row<T, D>(tile, 16 * rb + r, 32 * dc + 8 * g);
     }
@@ -392,7 +436,7 @@ struct LdsLane {
       return lds_frag_tr<T, D>(tile, 0, 16 * db, r, g);
 #else
       typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-      const uintptr_t base = reinterpret_cast<uintptr_t>(tile) + to[db];
+      const uintptr_t base = reinterpret_cast<uintptr_t>(tile) + tr_off(db);
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 16 * kRB));
       typename Elem<T>::frag o;
@@ -408,6 +452,17 @@ struct LdsLane {
     }
   }
 };
+
+// How tau reaches the two score-shaped tiles that carry it, S = tau Q K^T and
+// F = tau (U_Q K^T + Q U_K^T), in the BoB passes:
+//   kTauScaled  the resident operands hold X and tau X (tau X rounded to T); S uses
+//               X with the exp2 scale tau log2 e, F uses the scaled copies;
+//   kTauPow2    tau is a power of two, so tau X is exact and serves both tiles
+//               (exp2 scale log2 e) and X itself is not kept;
+//   kTauValu    the resident operands stay unscaled (one operand set fewer in
+//               registers); S uses the exp2 scale tau log2 e and the F tile is
+//               multiplied by tau on the VALU (one multiply per element).
+enum TauMode { kTauScaled = 0, kTauPow2 = 1, kTauValu = 2 };
 
 // Operand fragment scaled by s (fp32 product, rounded back to T).  Exact for
 // bf16 when s is a power of two.

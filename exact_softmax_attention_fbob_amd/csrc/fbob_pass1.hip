@@ -25,7 +25,11 @@
 // lane-local.  Row scalars enter as MFMA accumulator seeds (the dP tile starts at
 // -D, giving dP - D directly), tau is folded into the resident operands of the F
 // tile, and the row sums alpha and E' are MFMA contractions with a ones operand,
-// which leaves seven VALU operations plus one exp per score element.
+// which leaves seven VALU operations plus one exp per score element.  At d = 128
+// (twice the accumulators) the register budget of two waves per SIMD is met by
+// keeping the operands unscaled (tau applied to the F tile on the VALU), taking
+// the row sums as lane-local fp32 sums, and keeping one LDS offset per access
+// pattern.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -36,7 +40,7 @@
 namespace fbob {
 namespace {
 
-template <typename T, int D, int NW, int NI, bool FENCE, bool TP2, bool SKEW, int BC, bool DIRECT,
+template <typename T, int D, int NW, int NI, bool FENCE, int TM, bool SKEW, int BC, bool DIRECT,
           bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
@@ -73,9 +77,10 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
 
   // ---- resident row operands (B operand of the transposed score tiles) ----
   const int iw0 = rt * kBR + w * kRW;
-  // With TP2 (tau an exact power of two) tau Q is exact and also serves the
-  // score tile (S = (tau Q) K^T with exp2 scale log2 e); Q itself is not kept.
-  F qf[TP2 ? 1 : NI][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
+  // tqf / tuqf hold tau Q / tau U_Q, or Q / U_Q unscaled under kTauValu; qf (Q for
+  // the score tile) is a separate copy only under kTauScaled.
+  constexpr bool kQcopy = TM == kTauScaled;
+  F qf[kQcopy ? NI : 1][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
   float nl2[NI], dv[NI];
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
@@ -83,9 +88,10 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
 #pragma unroll
     for (int dc = 0; dc < kDC; ++dc) {
       const F q0 = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
-      if constexpr (!TP2) qf[ib][dc] = q0;
-      tqf[ib][dc] = scale_frag<T>(q0, tau);
-      tuqf[ib][dc] = scale_frag<T>(global_frag(UQh, i, N, D, 32 * dc + 8 * g), tau);
+      const F uq0 = global_frag(UQh, i, N, D, 32 * dc + 8 * g);
+      if constexpr (kQcopy) qf[ib][dc] = q0;
+      tqf[ib][dc] = TM == kTauValu ? q0 : scale_frag<T>(q0, tau);
+      tuqf[ib][dc] = TM == kTauValu ? uq0 : scale_frag<T>(uq0, tau);
       dof[ib][dc] = global_frag(dOh, i, N, D, 32 * dc + 8 * g);
     }
     nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
@@ -96,12 +102,19 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   // (r, g) therefore holds alpha of row r for g < 2 and E' for g >= 2.
   const F onesA = r < 8 ? ones_frag<T>() : zero_frag<T>();
   const F onesE = r < 8 ? zero_frag<T>() : ones_frag<T>();
+  // At d = 128 the registers of the two ones operands are worth more than the VALU
+  // adds: there the row sums are lane-local fp32 partial sums (keys 4 g + q of row
+  // r), reduced over the four lanes of a row at the end.
+  constexpr bool kVsum = D >= 128;
+  float asum[NI], esum[NI];
 
   f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
   f32x4 accAE[NI];
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
     accAE[ib] = splat4(0.f);
+    asum[ib] = 0.f;
+    esum[ib] = 0.f;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
       accB[ib][db] = splat4(0.f);
@@ -110,8 +123,9 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       accO[ib][db] = accB[ib][db];
     }
   }
-  const float c1 = TP2 ? kLog2e : tau * kLog2e;
-  const LdsLane<T, D> rd(r, g);
+  const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
+  // At d = 128 the lane keeps one LDS offset per access pattern (XOR form).
+  const LdsLane<T, D, (D >= 128)> rd(r, g);
 
   int jend = N;
   if (CAUSAL) jend = min(N, rt * kBR + kBR);
@@ -131,6 +145,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     const char* UKt = Kt + 2 * kTB;
     const char* UVt = Kt + 3 * kTB;
     const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > iw0);
+    const auto rx = rd.fresh();
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       f32x4 s[NI], t[NI], f[NI], gg[NI];
@@ -143,13 +158,13 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       }
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
-        const F kf = rd.row(Kt, jb, dc);
-        const F vf = rd.row(Vt, jb, dc);
-        const F ukf = rd.row(UKt, jb, dc);
-        const F uvf = rd.row(UVt, jb, dc);
+        const F kf = rx.row(Kt, jb, dc);
+        const F vf = rx.row(Vt, jb, dc);
+        const F ukf = rx.row(UKt, jb, dc);
+        const F uvf = rx.row(UVt, jb, dc);
 #pragma unroll
         for (int ib = 0; ib < NI; ++ib) {
-          s[ib] = E::mma(kf, TP2 ? tqf[ib][dc] : qf[TP2 ? 0 : ib][dc], s[ib]);
+          s[ib] = E::mma(kf, kQcopy ? qf[kQcopy ? ib : 0][dc] : tqf[ib][dc], s[ib]);
           f[ib] = E::mma(kf, tuqf[ib][dc], f[ib]);
           f[ib] = E::mma(ukf, tqf[ib][dc], f[ib]);
           t[ib] = E::mma(vf, dof[ib][dc], t[ib]);
@@ -158,6 +173,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       }
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
+        if constexpr (TM == kTauValu) f[ib] = tau * f[ib];
         f32x4 p;
 #pragma unroll
         for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[ib][q], c1, nl2[ib]));
@@ -172,10 +188,16 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
         // elements 4 jb .. 4 jb + 3 of the fragments
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const float pf = p[q] * f[ib][q];
+          const float pw = p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]);
           fr.p[ib][4 * jb + q] = (T)p[q];
           fr.ds[ib][4 * jb + q] = (T)(p[q] * t[ib][q]);
-          fr.pf[ib][4 * jb + q] = (T)(p[q] * f[ib][q]);
-          fr.pw[ib][4 * jb + q] = (T)(p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]));
+          fr.pf[ib][4 * jb + q] = (T)pf;
+          fr.pw[ib][4 * jb + q] = (T)pw;
+          if constexpr (kVsum) {
+            asum[ib] += pf;
+            esum[ib] += pw;
+          }
         }
       }
     }
@@ -187,18 +209,21 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     const char* UKt = Kt + 2 * kTB;
     const char* UVt = Kt + 3 * kTB;
     if constexpr (FENCE) FBOB_SCHED_FENCE();
+    const auto rx = rd.fresh();
+    if constexpr (!kVsum) {
 #pragma unroll
-    for (int ib = 0; ib < NI; ++ib) {
-      accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
-      accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
+      for (int ib = 0; ib < NI; ++ib) {
+        accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
+        accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
+      }
     }
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
       if constexpr (FENCE) FBOB_SCHED_FENCE();
-      const F kt = rd.tr(Kt, db);
-      const F ukt = rd.tr(UKt, db);
-      const F vt = rd.tr(Vt, db);
-      const F uvt = rd.tr(UVt, db);
+      const F kt = rx.tr(Kt, db);
+      const F ukt = rx.tr(UKt, db);
+      const F vt = rx.tr(Vt, db);
+      const F uvt = rx.tr(UVt, db);
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
         accB[ib][db] = E::mma(kt, fr.p[ib], accB[ib][db]);
@@ -302,8 +327,8 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   for (int ib = 0; ib < NI; ++ib) {
     const int i = iw0 + 16 * ib + r;
     // F carries tau through the scaled resident operands.
-    const float al = __shfl(accAE[ib][0], r);
-    const float edeg = __shfl(accAE[ib][0], 32 + r);
+    const float al = kVsum ? group_sum(asum[ib]) : __shfl(accAE[ib][0], r);
+    const float edeg = kVsum ? group_sum(esum[ib]) : __shfl(accAE[ib][0], 32 + r);
     if (i < N) {
       const int64_t ro = q_off + (int64_t)i * D;
 #pragma unroll
@@ -322,7 +347,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   }
 }
 
-template <typename T, int D, int NW, int NI, bool FENCE, bool TP2, bool SKEW = false, int BC = 32,
+template <typename T, int D, int NW, int NI, bool FENCE, int TM, bool SKEW = false, int BC = 32,
           bool DIRECT = false>
 hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
@@ -330,10 +355,10 @@ hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   const int total = n_row_tiles * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TP2, SKEW, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TM, SKEW, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,
                        a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TP2, SKEW, BC, DIRECT, false>), dim3(total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TM, SKEW, BC, DIRECT, false>), dim3(total), dim3(NW * 64), 0,
                        s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
 }
@@ -350,17 +375,24 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
     if (p.d == 64) {
       static const int cfg = tune_choice("FBOB_TUNE_P1");
       if (tau_is_pow2(p.tau)) {
-        if (cfg == 1) return launch_t<__bf16, 64, 8, 1, true, true, false, 32, true>(p, a, s);
-        if (cfg == 2) return launch_t<__bf16, 64, 8, 1, true, true, false, 32, false>(p, a, s);
-        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, false, true, false, 64, true>(p, a, s);
-        return launch_t<__bf16, 64, 8, 1, true, true, false, 64, true>(p, a, s);
+        if (cfg == 1) return launch_t<__bf16, 64, 8, 1, true, kTauPow2, false, 32, true>(p, a, s);
+        if (cfg == 2) return launch_t<__bf16, 64, 8, 1, true, kTauPow2, false, 32, false>(p, a, s);
+        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, false, kTauPow2, false, 64, true>(p, a, s);
+        return launch_t<__bf16, 64, 8, 1, true, kTauPow2, false, 64, true>(p, a, s);
       }
-      return launch_t<__bf16, 64, 8, 1, true, false>(p, a, s);
+      return launch_t<__bf16, 64, 8, 1, true, kTauValu, false, 64, true>(p, a, s);
     }
-    return launch_t<__bf16, 128, 4, 1, true, false>(p, a, s);
+    // d = 128: two waves per SIMD need the unscaled operands (kTauValu), the VALU row
+    // sums and the XOR-form LDS offsets to fit 256 registers; 32-key stages (64-key
+    // stages spill).  Alternatives: 1 no scheduling fences, 2 the one-wave-per-SIMD
+    // layout with tau-scaled operand copies.
+    static const int cfg = tune_choice("FBOB_TUNE_P1_D128");
+    if (cfg == 1) return launch_t<__bf16, 128, 8, 1, false, kTauValu, false, 32, true>(p, a, s);
+    if (cfg == 2) return launch_t<__bf16, 128, 4, 1, true, kTauScaled>(p, a, s);
+    return launch_t<__bf16, 128, 8, 1, true, kTauValu, false, 32, true>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 4, 1, true, false>(p, a, s);
-  return launch_t<float, 128, 4, 1, true, false>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 1, true, kTauScaled>(p, a, s);
+  return launch_t<float, 128, 4, 1, true, kTauValu>(p, a, s);
 }
 
 }  // namespace fbob

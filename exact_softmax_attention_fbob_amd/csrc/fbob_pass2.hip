@@ -36,7 +36,7 @@
 namespace fbob {
 namespace {
 
-template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, bool TP2, bool DIRECT, bool CAUSAL>
+template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, int TM, bool DIRECT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
                                                         float tau, int n_col_tiles, int total) {
   using E = Elem<T>;
@@ -65,18 +65,20 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   const T* UVh = reinterpret_cast<const T*>(a.UV) + kv_off;
 
   const int jw0 = ct * kBCw + w * kCW;
-  // With TP2 (tau an exact power of two) tau K is exact, so the score tile also
-  // uses it (S = Q (tau K)^T with exp2 scale log2 e) and K itself is not kept.
-  F kf[TP2 ? 1 : NJ][kDC], tkf[NJ][kDC], tukf[NJ][kDC], vf[NJ][kDC], uvf[NJ][kDC];
+  // tkf / tukf hold tau K / tau U_K, or K / U_K unscaled under kTauValu; kf (K for
+  // the score tile) is a separate copy only under kTauScaled.
+  constexpr bool kKcopy = TM == kTauScaled;
+  F kf[kKcopy ? NJ : 1][kDC], tkf[NJ][kDC], tukf[NJ][kDC], vf[NJ][kDC], uvf[NJ][kDC];
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
     for (int dc = 0; dc < kDC; ++dc) {
       const int j = jw0 + 16 * jb + r, col = 32 * dc + 8 * g;
       const F k0 = global_frag(Kh, j, N, D, col);
-      if constexpr (!TP2) kf[jb][dc] = k0;
-      tkf[jb][dc] = scale_frag<T>(k0, tau);
-      tukf[jb][dc] = scale_frag<T>(global_frag(UKh, j, N, D, col), tau);
+      const F uk0 = global_frag(UKh, j, N, D, col);
+      if constexpr (kKcopy) kf[jb][dc] = k0;
+      tkf[jb][dc] = TM == kTauValu ? k0 : scale_frag<T>(k0, tau);
+      tukf[jb][dc] = TM == kTauValu ? uk0 : scale_frag<T>(uk0, tau);
       vf[jb][dc] = global_frag(Vh, j, N, D, col);
       uvf[jb][dc] = global_frag(UVh, j, N, D, col);
     }
@@ -89,7 +91,10 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       accK[jb][db] = splat4(0.f);
       accV[jb][db] = accK[jb][db];
     }
-  const float c1 = TP2 ? kLog2e : tau * kLog2e;
+  const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
+  // Under kTauValu the F - alpha tile accumulates F / tau - alpha / tau and is scaled
+  // by tau afterwards, so its seed is -alpha / tau.
+  const float inv_tau = TM == kTauValu ? 1.f / tau : 1.f;
   const LdsLane<T, D> rd(r, g);
 
   // Row steps: (query head of the group, row chunk); causal rows start at the
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
     if (tid < BRS) {
       const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
       const float L = a.L[ri], Dv = a.D[ri], al = a.alpha[ri], Ev = a.E[ri];
-      scal = f32x4{-L * kLog2e, -Dv, -al, -(Ev + al * Dv)};
+      scal = f32x4{-L * kLog2e, -Dv, -al * inv_tau, -(Ev + al * Dv)};
     }
   };
   auto store_step = [&](char* buf) {
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
         const F uqa = rd.row(UQt, 2 * sc + ib, dc);
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
-          s[jb] = E::mma(qa, TP2 ? tkf[jb][dc] : kf[TP2 ? 0 : jb][dc], s[jb]);
+          s[jb] = E::mma(qa, kKcopy ? kf[kKcopy ? jb : 0][dc] : tkf[jb][dc], s[jb]);
           u[jb] = E::mma(uqa, tkf[jb][dc], u[jb]);
           u[jb] = E::mma(qa, tukf[jb][dc], u[jb]);
           t[jb] = E::mma(doa, vf[jb][dc], t[jb]);
@@ -174,6 +179,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       }
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb) {
+        if constexpr (TM == kTauValu) u[jb] = tau * u[jb];
         f32x4 p;
 #pragma unroll
         for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[jb][q], c1, nL[q]));
@@ -250,17 +256,17 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   }
 }
 
-template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, bool TP2, bool DIRECT = false>
+template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, int TM, bool DIRECT = false>
 hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   constexpr int kBCw = NW * 16 * NJ;
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
   const int total = n_col_tiles * p.B * p.Hkv;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TP2, DIRECT, true>), dim3(total), dim3(NW * 64),
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TM, DIRECT, true>), dim3(total), dim3(NW * 64),
                        0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   else
-    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TP2, DIRECT, false>), dim3(total), dim3(NW * 64),
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TM, DIRECT, false>), dim3(total), dim3(NW * 64),
                        0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   return hipGetLastError();
 }
@@ -277,17 +283,24 @@ hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
     if (p.d == 64) {
       static const int cfg = tune_choice("FBOB_TUNE_P2");
       if (tau_is_pow2(p.tau)) {
-        if (cfg == 1) return launch_t<__bf16, 64, 8, 2, 64, false, true, false>(p, a, s);
-        if (cfg == 2) return launch_t<__bf16, 64, 8, 2, 64, true, true, true>(p, a, s);
-        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 64, true, true, false>(p, a, s);
-        return launch_t<__bf16, 64, 8, 2, 64, false, true, true>(p, a, s);
+        if (cfg == 1) return launch_t<__bf16, 64, 8, 2, 64, false, kTauPow2, false>(p, a, s);
+        if (cfg == 2) return launch_t<__bf16, 64, 8, 2, 64, true, kTauPow2, true>(p, a, s);
+        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 64, true, kTauPow2, false>(p, a, s);
+        return launch_t<__bf16, 64, 8, 2, 64, false, kTauPow2, true>(p, a, s);
       }
-      return launch_t<__bf16, 64, 8, 1, 64, true, false>(p, a, s);
+      return launch_t<__bf16, 64, 8, 2, 64, false, kTauValu, true>(p, a, s);
     }
-    return launch_t<__bf16, 128, 4, 1, 32, true, false>(p, a, s);
+    // d = 128: unscaled operands (kTauValu) for two waves per SIMD, 64-row stages.
+    // Alternatives: 1 with scheduling fences, 2 the one-wave-per-SIMD layout with
+    // tau-scaled operand copies, 3 32-row stages.
+    static const int cfg = tune_choice("FBOB_TUNE_P2_D128");
+    if (cfg == 1) return launch_t<__bf16, 128, 8, 1, 64, true, kTauValu, true>(p, a, s);
+    if (cfg == 2) return launch_t<__bf16, 128, 4, 1, 32, true, kTauScaled>(p, a, s);
+    if (cfg == 3) return launch_t<__bf16, 128, 8, 1, 32, true, kTauValu, true>(p, a, s);
+    return launch_t<__bf16, 128, 8, 1, 64, false, kTauValu, true>(p, a, s);
   }
-  if (p.d == 64) return launch_t<float, 64, 4, 1, 32, true, false>(p, a, s);
-  return launch_t<float, 128, 4, 1, 32, true, false>(p, a, s);
+  if (p.d == 64) return launch_t<float, 64, 4, 1, 32, true, kTauScaled>(p, a, s);
+  return launch_t<float, 128, 4, 1, 32, true, kTauValu>(p, a, s);
 }
 
 }  // namespace fbob
