@@ -37,6 +37,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 #endif
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Instruction groups for __builtin_amdgcn_sched_group_barrier: the scheduler
+// fills the groups in the order they are declared (one pipeline per region), so a
+// sequence of (LDS read, n) and (MFMA, m) groups fixes how far fragment loads run
+// ahead of the MFMAs that consume them.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+#define FBOB_SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // ---------------------------------------------------------------------------
 // Element traits: storage type of the seven inputs.
 // ---------------------------------------------------------------------------

@@ -40,12 +40,16 @@
 namespace fbob {
 namespace {
 
-template <typename T, int D, int NW, int NI, bool FENCE, int TM, bool SKEW, int BC, bool DIRECT,
-          bool CAUSAL>
+// SCHED: 0 leaves instruction order to the compiler, 1 fences each phase and
+// column block (sched_barrier), 2 double-buffers the LDS fragments one step ahead
+// of the MFMAs that use them, with the order pinned by sched_group_barrier.
+template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
+  constexpr bool FENCE = SCHED == 1;
+  constexpr bool kPipe = SCHED == 2;
   constexpr int kThreads = NW * 64;
   constexpr int kRW = 16 * NI;                       // query rows per wave
   constexpr int kBR = NW * kRW;                      // query rows per work-group
@@ -53,8 +57,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   constexpr int kTB = kBC * Tile<T, D>::kRowBytes;   // bytes per staged tile
   constexpr int kDC = D / 32;
   constexpr int kDB = D / 16;
-  constexpr int kSlots = SKEW ? 3 : 2;  // LDS ring depth
-  __shared__ __attribute__((aligned(16))) char lds[kSlots][4 * kTB];
+  __shared__ __attribute__((aligned(16))) char lds[2][4 * kTB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   // At d = 128 the registers of the two ones operands are worth more than the VALU
   // adds: there the row sums are lane-local fp32 partial sums (keys 4 g + q of row
   // r), reduced over the four lanes of a row at the end.
-  constexpr bool kVsum = D >= 128;
+  constexpr bool kVsum = D >= 128 || NI >= 2;
   float asum[NI], esum[NI];
 
   f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   }
   const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
   // At d = 128 the lane keeps one LDS offset per access pattern (XOR form).
-  const LdsLane<T, D, (D >= 128)> rd(r, g);
+  const LdsLane<T, D, (D >= 128 || NI >= 2)> rd(r, g);
 
   int jend = N;
   if (CAUSAL) jend = min(N, rt * kBR + kBR);
@@ -140,12 +143,28 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   // the K, V, U_K, U_V fragments of a block serve every row block of the wave.
   // The bounds / causal test runs only on edge tiles (a wave-uniform branch
   // around the P values).
-  auto score_phase = [&](const char* Kt, int j0, Frags& fr) {
+  // `edge_tag` is a bool (runtime test) or std::true_type / std::false_type (the
+  // test resolved at compile time: a separate straight-line copy).
+  auto score_body = [&](const char* Kt, int j0, Frags& fr, auto edge_tag) {
+    const bool edge = edge_tag;
     const char* Vt = Kt + kTB;
     const char* UKt = Kt + 2 * kTB;
     const char* UVt = Kt + 3 * kTB;
-    const bool edge = (j0 + kBC > N) || (CAUSAL && j0 + kBC - 1 > iw0);
     const auto rx = rd.fresh();
+    // kPipe: the four fragments of (jb, dc) step it + 1 are read while step it's
+    // MFMAs run (two register slots, alternating).
+    constexpr int kSteps = 2 * kDC;
+    F pk[2], pv[2], puk[2], puv[2];
+    auto rowload = [&](int it, int sl) {
+      pk[sl] = rx.row(Kt, it / kDC, it % kDC);
+      pv[sl] = rx.row(Vt, it / kDC, it % kDC);
+      puk[sl] = rx.row(UKt, it / kDC, it % kDC);
+      puv[sl] = rx.row(UVt, it / kDC, it % kDC);
+    };
+    if constexpr (kPipe) {
+      rowload(0, 0);
+      FBOB_SGB(kSgDsRead, 4);
+    }
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       f32x4 s[NI], t[NI], f[NI], gg[NI];
@@ -158,10 +177,23 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       }
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
-        const F kf = rx.row(Kt, jb, dc);
-        const F vf = rx.row(Vt, jb, dc);
-        const F ukf = rx.row(UKt, jb, dc);
-        const F uvf = rx.row(UVt, jb, dc);
+        const int it = jb * kDC + dc, sl = it & 1;
+        F kf, vf, ukf, uvf;
+        if constexpr (kPipe) {
+          if (it + 1 < kSteps) {
+            rowload(it + 1, sl ^ 1);
+            FBOB_SGB(kSgDsRead, 4);
+          }
+          kf = pk[sl];
+          vf = pv[sl];
+          ukf = puk[sl];
+          uvf = puv[sl];
+        } else {
+          kf = rx.row(Kt, jb, dc);
+          vf = rx.row(Vt, jb, dc);
+          ukf = rx.row(UKt, jb, dc);
+          uvf = rx.row(UVt, jb, dc);
+        }
 #pragma unroll
         for (int ib = 0; ib < NI; ++ib) {
           s[ib] = E::mma(kf, kQcopy ? qf[kQcopy ? ib : 0][dc] : tqf[ib][dc], s[ib]);
@@ -170,6 +202,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
           t[ib] = E::mma(vf, dof[ib][dc], t[ib]);
           gg[ib] = E::mma(uvf, dof[ib][dc], gg[ib]);
         }
+        if constexpr (kPipe) FBOB_SGB(kSgMfma, 5 * NI);
       }
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
@@ -202,6 +235,18 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       }
     }
   };
+  // Under kPipe the bounds / causal test is compiled into a separate copy of the
+  // tile body that only edge tiles take, so the pinned schedule spans one
+  // straight-line region; otherwise it is a wave-uniform branch inside the body.
+  auto score_phase = [&](const char* Kt, int j0, Frags& fr) {
+    const bool edge = (j0 + 32 > N) || (CAUSAL && j0 + 31 > iw0);
+    if constexpr (kPipe) {
+      if (edge) score_body(Kt, j0, fr, std::true_type{});
+      else score_body(Kt, j0, fr, std::false_type{});
+    } else {
+      score_body(Kt, j0, fr, edge);
+    }
+  };
 
   // Contractions over the tile's keys (transposed outputs) and the row sums.
   auto output_phase = [&](const char* Kt, const Frags& fr) {
@@ -216,14 +261,41 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
         accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
         accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
       }
+      if constexpr (kPipe) FBOB_SGB(kSgMfma, 2 * NI);
+    }
+    // kPipe: the transposed fragments of column block db + 1 are read while
+    // block db's MFMAs run (two register slots; each read is two instructions).
+    F tk[2], tuk[2], tv[2], tuv[2];
+    auto trload = [&](int db, int sl) {
+      tk[sl] = rx.tr(Kt, db);
+      tuk[sl] = rx.tr(UKt, db);
+      tv[sl] = rx.tr(Vt, db);
+      tuv[sl] = rx.tr(UVt, db);
+    };
+    if constexpr (kPipe) {
+      trload(0, 0);
+      FBOB_SGB(kSgDsRead, 8);
     }
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
       if constexpr (FENCE) FBOB_SCHED_FENCE();
-      const F kt = rx.tr(Kt, db);
-      const F ukt = rx.tr(UKt, db);
-      const F vt = rx.tr(Vt, db);
-      const F uvt = rx.tr(UVt, db);
+      F kt, ukt, vt, uvt;
+      if constexpr (kPipe) {
+        const int sl = db & 1;
+        if (db + 1 < kDB) {
+          trload(db + 1, sl ^ 1);
+          FBOB_SGB(kSgDsRead, 8);
+        }
+        kt = tk[sl];
+        ukt = tuk[sl];
+        vt = tv[sl];
+        uvt = tuv[sl];
+      } else {
+        kt = rx.tr(Kt, db);
+        ukt = rx.tr(UKt, db);
+        vt = rx.tr(Vt, db);
+        uvt = rx.tr(UVt, db);
+      }
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
         accB[ib][db] = E::mma(kt, fr.p[ib], accB[ib][db]);
@@ -233,6 +305,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
         accO[ib][db] = E::mma(vt, fr.pf[ib], accO[ib][db]);
         accO[ib][db] = E::mma(uvt, fr.p[ib], accO[ib][db]);
       }
+      if constexpr (kPipe) FBOB_SGB(kSgMfma, 6 * NI);
     }
   };
 
@@ -273,53 +346,21 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     }
   };
 
-  if constexpr (!SKEW) {
-    // One pipeline step: prefetch tile t+1, compute tile t from `cur`, publish
-    // tile t+1 in `nxt`, barrier.  Unrolled by two so that both LDS buffers are
-    // compile-time addresses.
-    auto step = [&](int t, char* cur, char* nxt) {
-      const int j0 = t * kBC;
-      const bool more = t + 1 < ntc;
-      if (more) stage_load(nxt, j0 + kBC);
-      if (active_tile(t)) compute_stage(cur, j0);
-      if (more) stage_commit(nxt);
-      __syncthreads();
-    };
+  // One pipeline step: prefetch tile t+1, compute tile t from `cur`, publish
+  // tile t+1 in `nxt`, barrier.  Unrolled by two so that both LDS buffers are
+  // compile-time addresses.
+  auto step = [&](int t, char* cur, char* nxt) {
+    const int j0 = t * kBC;
+    const bool more = t + 1 < ntc;
+    if (more) stage_load(nxt, j0 + kBC);
+    if (active_tile(t)) compute_stage(cur, j0);
+    if (more) stage_commit(nxt);
+    __syncthreads();
+  };
 #pragma unroll 1
-    for (int t = 0; t < ntc; t += 2) {
-      step(t, lds[0], lds[1]);
-      if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
-    }
-  } else {
-    // Phase-skewed schedule.  The two waves sharing a SIMD (w and w + NW/2) run
-    // half a tile apart: the late group contracts tile t-1 while it builds the
-    // fragments of tile t, so one wave's elementwise work overlaps the other's
-    // contractions.  A three-slot LDS ring keeps tile t-1 resident for it.
-    const bool late = w >= NW / 2;
-    Frags held;
-    static_assert(!SKEW || BC == 32, "the skewed schedule works on 32-key stages");
-    auto step = [&](int t, const char* prev, char* cur, char* nxt) {
-      const int j0 = t * kBC;
-      const bool more = t + 1 < ntc;
-      if (more) stage_load(nxt, j0 + kBC);
-      if (late) {
-        if (t > 0 && active_tile(t - 1)) output_phase(prev, held);
-        if (active_tile(t)) score_phase(cur, j0, held);
-      } else if (active_tile(t)) {
-        Frags fr;
-        score_phase(cur, j0, fr);
-        output_phase(cur, fr);
-      }
-      if (more) stage_commit(nxt);
-      __syncthreads();
-    };
-#pragma unroll 1
-    for (int t = 0; t < ntc; t += 3) {
-      step(t, lds[2], lds[0], lds[1]);
-      if (t + 1 < ntc) step(t + 1, lds[0], lds[1], lds[2]);
-      if (t + 2 < ntc) step(t + 2, lds[1], lds[2], lds[0]);
-    }
-    if (late && active_tile(ntc - 1)) output_phase(lds[(ntc - 1) % 3], held);
+  for (int t = 0; t < ntc; t += 2) {
+    step(t, lds[0], lds[1]);
+    if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
   }
 
   // ---- row correction and the single write of each row output ----
@@ -347,18 +388,17 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   }
 }
 
-template <typename T, int D, int NW, int NI, bool FENCE, int TM, bool SKEW = false, int BC = 32,
-          bool DIRECT = false>
+template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC = 32, bool DIRECT = false>
 hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
   const int total = n_row_tiles * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TM, SKEW, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,
                        a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, FENCE, TM, SKEW, BC, DIRECT, false>), dim3(total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false>), dim3(total), dim3(NW * 64), 0,
                        s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
 }
@@ -373,23 +413,24 @@ int tune_choice(const char* name) {
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.bf16) {
     if (p.d == 64) {
-      static const int cfg = tune_choice("FBOB_TUNE_P1");
+      const int cfg = tune_choice("FBOB_TUNE_P1");
       if (tau_is_pow2(p.tau)) {
-        if (cfg == 1) return launch_t<__bf16, 64, 8, 1, true, kTauPow2, false, 32, true>(p, a, s);
-        if (cfg == 2) return launch_t<__bf16, 64, 8, 1, true, kTauPow2, false, 32, false>(p, a, s);
-        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, false, kTauPow2, false, 64, true>(p, a, s);
-        return launch_t<__bf16, 64, 8, 1, true, kTauPow2, false, 64, true>(p, a, s);
+        if (cfg == 1) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 64, true>(p, a, s);
+        if (cfg == 2) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 32, true>(p, a, s);
+        if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 32, false>(p, a, s);
+        if (cfg == 4) return launch_t<__bf16, 64, 8, 1, 0, kTauPow2, 64, true>(p, a, s);
+        return launch_t<__bf16, 64, 8, 1, 2, kTauPow2, 64, true>(p, a, s);
       }
-      return launch_t<__bf16, 64, 8, 1, true, kTauValu, false, 64, true>(p, a, s);
+      return launch_t<__bf16, 64, 8, 1, true, kTauValu, 64, true>(p, a, s);
     }
     // d = 128: two waves per SIMD need the unscaled operands (kTauValu), the VALU row
     // sums and the XOR-form LDS offsets to fit 256 registers; 32-key stages (64-key
     // stages spill).  Alternatives: 1 no scheduling fences, 2 the one-wave-per-SIMD
     // layout with tau-scaled operand copies.
-    static const int cfg = tune_choice("FBOB_TUNE_P1_D128");
-    if (cfg == 1) return launch_t<__bf16, 128, 8, 1, false, kTauValu, false, 32, true>(p, a, s);
+    const int cfg = tune_choice("FBOB_TUNE_P1_D128");
+    if (cfg == 1) return launch_t<__bf16, 128, 8, 1, false, kTauValu, 32, true>(p, a, s);
     if (cfg == 2) return launch_t<__bf16, 128, 4, 1, true, kTauScaled>(p, a, s);
-    return launch_t<__bf16, 128, 8, 1, true, kTauValu, false, 32, true>(p, a, s);
+    return launch_t<__bf16, 128, 8, 1, true, kTauValu, 32, true>(p, a, s);
   }
   if (p.d == 64) return launch_t<float, 64, 4, 1, true, kTauScaled>(p, a, s);
   return launch_t<float, 128, 4, 1, true, kTauValu>(p, a, s);

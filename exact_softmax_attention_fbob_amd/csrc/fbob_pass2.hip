@@ -281,7 +281,7 @@ int tune_choice(const char* name) {
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
   if (p.bf16) {
     if (p.d == 64) {
-      static const int cfg = tune_choice("FBOB_TUNE_P2");
+      const int cfg = tune_choice("FBOB_TUNE_P2");
       if (tau_is_pow2(p.tau)) {
         if (cfg == 1) return launch_t<__bf16, 64, 8, 2, 64, false, kTauPow2, false>(p, a, s);
         if (cfg == 2) return launch_t<__bf16, 64, 8, 2, 64, true, kTauPow2, true>(p, a, s);
@@ -293,7 +293,7 @@ hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
     // d = 128: unscaled operands (kTauValu) for two waves per SIMD, 64-row stages.
     // Alternatives: 1 with scheduling fences, 2 the one-wave-per-SIMD layout with
     // tau-scaled operand copies, 3 32-row stages.
-    static const int cfg = tune_choice("FBOB_TUNE_P2_D128");
+    const int cfg = tune_choice("FBOB_TUNE_P2_D128");
     if (cfg == 1) return launch_t<__bf16, 128, 8, 1, 64, true, kTauValu, true>(p, a, s);
     if (cfg == 2) return launch_t<__bf16, 128, 4, 1, 32, true, kTauScaled>(p, a, s);
     if (cfg == 3) return launch_t<__bf16, 128, 8, 1, 32, true, kTauValu, true>(p, a, s);

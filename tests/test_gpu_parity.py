@@ -172,3 +172,27 @@ def test_n1m_single_head_sampled_rows_and_invariants():
     gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
     _check_sampled_rows(w, inp, gpu, n_rows=8)
     _check_invariants(gpu)
+
+
+# Every compiled Pass 1 / Pass 2 variant that an environment override can select
+# (read by the library at each launch) against the oracle: a ragged case and a
+# causal grouped-query case at the variant's head dimension.
+TUNE_VARIANTS = [("FBOB_TUNE_P1", v) for v in (1, 2, 3, 4)] + \
+    [("FBOB_TUNE_P2", v) for v in (1, 2, 3)] + \
+    [("FBOB_TUNE_P1_D128", v) for v in (1, 2)] + \
+    [("FBOB_TUNE_P2_D128", v) for v in (1, 2, 3)]
+
+
+@pytest.mark.parametrize("var,val", TUNE_VARIANTS, ids=[f"{a}={b}" for a, b in TUNE_VARIANTS])
+def test_tuning_variants_match_oracle(var, val, monkeypatch):
+    d = 128 if var.endswith("D128") else 64
+    monkeypatch.setenv(var, str(val))
+    for w in (case(f"tune_n300_b2_h2_d{d}", 2, 2, 300, d, "bf16", 71),
+              case(f"tune_gqa_hq4_hkv2_n200_d{d}_causal", 1, 4, 200, d, "bf16", 72, causal=True,
+                   Hkv=2)):
+        U.say(f"[parity] {var}={val} {w.name}")
+        inp = U.make_inputs(w)
+        gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+        errs = U.compare_full(gpu, U.oracle_full(inp, w), w, keys=U.ALL_KEYS)
+        U.say(f"[parity] {var}={val} {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
