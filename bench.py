@@ -327,6 +327,10 @@ def main():
     p1_ms = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     p2_ms = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     bob_ms = np.mean([e[1].elapsed_time(e[3]) for e in evs])
+    med = {"fwd_stats": float(np.median([e[0].elapsed_time(e[1]) for e in evs])),
+           "bob_pass1": float(np.median([e[1].elapsed_time(e[2]) for e in evs])),
+           "bob_pass2": float(np.median([e[2].elapsed_time(e[3]) for e in evs])),
+           "bob": float(np.median([e[1].elapsed_time(e[3]) for e in evs]))}
     ms_step = wall * 1e3 / args.steps
 
     peak_mib = round(torch.cuda.max_memory_allocated(dev) / 2**20, 1)  # the step's own peak
@@ -361,6 +365,7 @@ def main():
         "bob_pct_bf16_peak": round(100 * bob_tflops / PEAK_TFLOPS["bf16"], 2),
         "kernels_ms": {"fwd_stats": round(float(fwd_ms), 4), "bob_pass1": round(float(p1_ms), 4),
                        "bob_pass2": round(float(p2_ms), 4)},
+        "median_ms": {k: round(v, 4) for k, v in med.items()},
         "flop_formula": "per (b,h): forward 4 N^2 d, pass1 22 N^2 d, pass2 16 N^2 d"
                         + ("; causal counts N(N+1)/2 of the N^2 pairs" if causal else ""),
         "peak_mem_mib": peak_mib,

@@ -19,8 +19,10 @@ pytestmark = pytest.mark.gpu
 W = workloads.WORKLOADS
 
 
-def case(name, B, H, N, d, dtype, seed, causal=False, Hkv=None, **kw):
+def case(name, B, H, N, d, dtype, seed, causal=False, Hkv=None, tau=None, **kw):
     extra = {"Hkv": Hkv} if Hkv else {}
+    if tau is not None:
+        extra["tau"] = tau
     return workloads.Workload(name, B=B, H=H, N=N, d=d, dtype=dtype, seed=seed, causal=causal,
                               extra=extra, **kw)
 
@@ -35,6 +37,7 @@ CASES = [
     case("g_gqa_hq6_hkv2_n160_bf16_causal", 1, 6, 160, 64, "bf16", 47, causal=True, Hkv=2),
     case("g_mqa_hq3_hkv1_n96_d128_bf16", 1, 3, 96, 128, "bf16", 48, Hkv=1),
     case("g_n1000_qk2_bf16", 1, 1, 1000, 64, "bf16", 49, scale_qk=2.0),
+    case("g_n210_h2_bf16_tau0.1_causal", 1, 2, 210, 64, "bf16", 52, causal=True, tau=0.1),
 ]
 
 

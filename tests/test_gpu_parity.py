@@ -18,8 +18,10 @@ pytestmark = pytest.mark.gpu
 W = workloads.WORKLOADS
 
 
-def case(name, B, H, N, d, dtype, seed, causal=False, Hkv=None, **kw):
+def case(name, B, H, N, d, dtype, seed, causal=False, Hkv=None, tau=None, **kw):
     extra = {"Hkv": Hkv} if Hkv else {}
+    if tau is not None:
+        extra["tau"] = tau
     return workloads.Workload(name, B=B, H=H, N=N, d=d, dtype=dtype, seed=seed, causal=causal,
                               extra=extra, **kw)
 
@@ -38,6 +40,11 @@ SMALL = [
     case("gqa_hq6_hkv2_n160_bf16_causal", 1, 6, 160, 64, "bf16", 20, causal=True, Hkv=2),
     case("mqa_hq3_hkv1_n96_d128_bf16", 1, 3, 96, 128, "bf16", 21, Hkv=1),
     case("n1000_u01_qk2_bf16", 1, 1, 1000, 64, "bf16", 22, scale_u=0.1, scale_qk=2.0),
+    # a score scale that is not a power of two at d = 64 (tau applied on the VALU)
+    case("n250_h2_bf16_tau0.1", 1, 2, 250, 64, "bf16", 23, tau=0.1),
+    case("n190_h2_bf16_tau0.3_causal", 1, 2, 190, 64, "bf16", 24, causal=True, tau=0.3),
+    case("n160_d128_bf16_tau0.25", 1, 1, 160, 128, "bf16", 25, tau=0.25),
+    case("n90_f32_tau0.2", 1, 1, 90, 64, "f32", 26, tau=0.2),
 ]
 
 

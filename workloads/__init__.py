@@ -38,7 +38,8 @@ class Workload:
 
     @property
     def tau(self) -> float:
-        return 1.0 / math.sqrt(self.d)
+        """Score scale: 1/sqrt(d) unless the workload sets extra["tau"]."""
+        return float(self.extra.get("tau", 1.0 / math.sqrt(self.d)))
 
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
