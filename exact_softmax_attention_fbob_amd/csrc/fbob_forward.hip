@@ -14,6 +14,8 @@
 // maximum exceeds it by more than kSlack (weights then stay <= 2^kSlack), so the
 // accumulator rescale is rare.  The row sum of the weights is an MFMA contraction
 // with a ones operand over the same bf16 weights that multiply V.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "fbob_device.hpp"
@@ -191,7 +193,13 @@ hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
       if (tau_is_pow2(p.tau)) return launch_t<__bf16, 64, 8, 64, true>(p, a, s);
       return launch_t<__bf16, 64, 8, 64, false>(p, a, s);
     }
-    return launch_t<__bf16, 128, 8, 32, false>(p, a, s);
+    const char* v = getenv("FBOB_TUNE_FWD_D128");
+    const int cfg = v ? atoi(v) : 0;
+    // d = 128: 64-key stages (measured ~2 % faster than 32); 1 and 2 select 32-key
+    // stages with 8 or 4 waves per work-group.
+    if (cfg == 1) return launch_t<__bf16, 128, 8, 32, false>(p, a, s);
+    if (cfg == 2) return launch_t<__bf16, 128, 4, 32, false>(p, a, s);
+    return launch_t<__bf16, 128, 8, 64, false>(p, a, s);
   }
   if (p.d == 64) return launch_t<float, 64, 4, 32, false>(p, a, s);
   return launch_t<float, 128, 4, 32, false>(p, a, s);
