@@ -45,6 +45,23 @@ constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
 #define FBOB_SGB(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
+// Wave priority around an MFMA-dense block: while one wave of a SIMD issues its
+// MFMAs at raised priority the matrix pipe stays fed, and the other wave's VALU
+// work fills the issue cycles in between.  The scheduling fences keep the block's
+// instructions between the two priority changes.
+#define FBOB_PRIO_HIGH()               \
+  do {                                 \
+    __builtin_amdgcn_sched_barrier(0); \
+    __builtin_amdgcn_s_setprio(1);     \
+    __builtin_amdgcn_sched_barrier(0); \
+  } while (0)
+#define FBOB_PRIO_LOW()                \
+  do {                                 \
+    __builtin_amdgcn_sched_barrier(0); \
+    __builtin_amdgcn_s_setprio(0);     \
+    __builtin_amdgcn_sched_barrier(0); \
+  } while (0)
+
 // ---------------------------------------------------------------------------
 // Element traits: storage type of the seven inputs.
 // ---------------------------------------------------------------------------

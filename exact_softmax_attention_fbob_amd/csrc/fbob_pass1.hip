@@ -42,14 +42,18 @@ namespace {
 
 // SCHED: 0 leaves instruction order to the compiler, 1 fences each phase and
 // column block (sched_barrier), 2 double-buffers the LDS fragments one step ahead
-// of the MFMAs that use them, with the order pinned by sched_group_barrier.
+// of the MFMAs that use them, with the order pinned by sched_group_barrier; 3 is 2
+// with raised wave priority over the contraction MFMAs, 4 also over the score
+// MFMAs.
 template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr bool FENCE = SCHED == 1;
-  constexpr bool kPipe = SCHED == 2;
+  constexpr bool kPipe = SCHED >= 2;
+  constexpr bool kPrioOut = SCHED >= 3;
+  constexpr bool kPrioScore = SCHED >= 4;
   constexpr int kThreads = NW * 64;
   constexpr int kRW = 16 * NI;                       // query rows per wave
   constexpr int kBR = NW * kRW;                      // query rows per work-group
@@ -175,6 +179,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
         f[ib] = splat4(0.f);
         gg[ib] = splat4(0.f);
       }
+      if constexpr (kPrioScore) FBOB_PRIO_HIGH();
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
         const int it = jb * kDC + dc, sl = it & 1;
@@ -204,6 +209,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
         }
         if constexpr (kPipe) FBOB_SGB(kSgMfma, 5 * NI);
       }
+      if constexpr (kPrioScore) FBOB_PRIO_LOW();
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
         if constexpr (TM == kTauValu) f[ib] = tau * f[ib];
@@ -254,6 +260,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     const char* UKt = Kt + 2 * kTB;
     const char* UVt = Kt + 3 * kTB;
     if constexpr (FENCE) FBOB_SCHED_FENCE();
+    if constexpr (kPrioOut) FBOB_PRIO_HIGH();
     const auto rx = rd.fresh();
     if constexpr (!kVsum) {
 #pragma unroll
@@ -307,6 +314,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       }
       if constexpr (kPipe) FBOB_SGB(kSgMfma, 6 * NI);
     }
+    if constexpr (kPrioOut) FBOB_PRIO_LOW();
   };
 
   // Staging: registers + ds_write (MultiStager) or direct global -> LDS.
@@ -419,7 +427,9 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
         if (cfg == 2) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 32, true>(p, a, s);
         if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 32, false>(p, a, s);
         if (cfg == 4) return launch_t<__bf16, 64, 8, 1, 0, kTauPow2, 64, true>(p, a, s);
-        return launch_t<__bf16, 64, 8, 1, 2, kTauPow2, 64, true>(p, a, s);
+        if (cfg == 5) return launch_t<__bf16, 64, 8, 1, 2, kTauPow2, 64, true>(p, a, s);
+        if (cfg == 6) return launch_t<__bf16, 64, 8, 1, 4, kTauPow2, 64, true>(p, a, s);
+        return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
       }
       return launch_t<__bf16, 64, 8, 1, true, kTauValu, 64, true>(p, a, s);
     }

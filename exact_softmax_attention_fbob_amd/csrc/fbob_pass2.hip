@@ -36,11 +36,17 @@
 namespace fbob {
 namespace {
 
-template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, int TM, bool DIRECT, bool CAUSAL>
+// SCHED: 0 leaves instruction order to the compiler, 1 fences the phases and
+// column blocks; 3 raises the wave priority over the contraction MFMAs, 4 also over
+// the score MFMAs (no fences otherwise).
+template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DIRECT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
                                                         float tau, int n_col_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
+  constexpr bool FENCE = SCHED == 1;
+  constexpr bool kPrioOut = SCHED >= 3;
+  constexpr bool kPrioScore = SCHED >= 4;
   constexpr int kThreads = NW * 64;
   constexpr int kCW = 16 * NJ;                      // keys per wave
   constexpr int kBCw = NW * kCW;                    // keys per work-group
@@ -163,6 +169,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
         u[jb] = nA;
         gp[jb] = nG;
       }
+      if constexpr (kPrioScore) FBOB_PRIO_HIGH();
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
         const F qa = rd.row(Qt, 2 * sc + ib, dc);
@@ -177,6 +184,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
           gp[jb] = E::mma(doa, uvf[jb][dc], gp[jb]);
         }
       }
+      if constexpr (kPrioScore) FBOB_PRIO_LOW();
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb) {
         if constexpr (TM == kTauValu) u[jb] = tau * u[jb];
@@ -200,6 +208,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       }
     }
     if constexpr (FENCE) FBOB_SCHED_FENCE();
+    if constexpr (kPrioOut) FBOB_PRIO_HIGH();
     const char* Qs = Qt + 32 * sc * Tile<T, D>::kRowBytes;
     const char* dOs = dOt + 32 * sc * Tile<T, D>::kRowBytes;
     const char* UQs = UQt + 32 * sc * Tile<T, D>::kRowBytes;
@@ -216,6 +225,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
         accV[jb][db] = E::mma(dot, ddpB[jb], accV[jb][db]);
       }
     }
+    if constexpr (kPrioOut) FBOB_PRIO_LOW();
   };
 
   load_step(0, lds[0]);
@@ -256,17 +266,17 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   }
 }
 
-template <typename T, int D, int NW, int NJ, int BRS, bool FENCE, int TM, bool DIRECT = false>
+template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DIRECT = false>
 hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   constexpr int kBCw = NW * 16 * NJ;
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
   const int total = n_col_tiles * p.B * p.Hkv;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TM, DIRECT, true>), dim3(total), dim3(NW * 64),
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, true>), dim3(total), dim3(NW * 64),
                        0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   else
-    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, FENCE, TM, DIRECT, false>), dim3(total), dim3(NW * 64),
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, false>), dim3(total), dim3(NW * 64),
                        0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
   return hipGetLastError();
 }
@@ -286,7 +296,9 @@ hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
         if (cfg == 1) return launch_t<__bf16, 64, 8, 2, 64, false, kTauPow2, false>(p, a, s);
         if (cfg == 2) return launch_t<__bf16, 64, 8, 2, 64, true, kTauPow2, true>(p, a, s);
         if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 64, true, kTauPow2, false>(p, a, s);
-        return launch_t<__bf16, 64, 8, 2, 64, false, kTauPow2, true>(p, a, s);
+        if (cfg == 4) return launch_t<__bf16, 64, 8, 2, 64, 3, kTauPow2, true>(p, a, s);
+        if (cfg == 5) return launch_t<__bf16, 64, 8, 2, 64, 0, kTauPow2, true>(p, a, s);
+        return launch_t<__bf16, 64, 8, 2, 64, 4, kTauPow2, true>(p, a, s);
       }
       return launch_t<__bf16, 64, 8, 2, 64, false, kTauValu, true>(p, a, s);
     }

@@ -184,8 +184,8 @@ def test_n1m_single_head_sampled_rows_and_invariants():
 # Every compiled Pass 1 / Pass 2 variant that an environment override can select
 # (read by the library at each launch) against the oracle: a ragged case and a
 # causal grouped-query case at the variant's head dimension.
-TUNE_VARIANTS = [("FBOB_TUNE_P1", v) for v in (1, 2, 3, 4)] + \
-    [("FBOB_TUNE_P2", v) for v in (1, 2, 3)] + \
+TUNE_VARIANTS = [("FBOB_TUNE_P1", v) for v in (1, 2, 3, 4, 5, 6)] + \
+    [("FBOB_TUNE_P2", v) for v in (1, 2, 3, 4, 5)] + \
     [("FBOB_TUNE_P1_D128", v) for v in (1, 2)] + \
     [("FBOB_TUNE_P2_D128", v) for v in (1, 2, 3)] + \
     [("FBOB_TUNE_FWD_D128", v) for v in (1, 2)]
