@@ -204,3 +204,65 @@ def test_tuning_variants_match_oracle(var, val, monkeypatch):
         errs = U.compare_full(gpu, U.oracle_full(inp, w), w, keys=U.ALL_KEYS)
         U.say(f"[parity] {var}={val} {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
         assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+
+
+def test_runs_on_a_side_stream():
+    """Every call is issued on torch's current stream: run the whole path on a side
+    stream and compare with the default-stream results bitwise."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    w = case("stream_n320_h2_bf16", 1, 2, 320, 64, "bf16", 33)
+    U.say(f"[parity] {w.name}")
+    dev = U.to_device(U.make_inputs(w), w.dtype)
+    args = (dev["Q"], dev["K"], dev["V"], dev["dO"], dev["UQ"], dev["UK"], dev["UV"])
+    O, L, D = fb.forward(*args[:4], w.tau)
+    ref = fb.bob(*args, O, L, D, w.tau)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        O2, L2, D2 = fb.forward(*args[:4], w.tau)
+        got = fb.bob(*args, O2, L2, D2, w.tau)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(L, L2) and torch.equal(D, D2)
+    for k in ref:
+        assert torch.equal(ref[k], got[k]), k
+
+
+def test_hip_graph_capture_and_replay():
+    """The library allocates nothing and issues no memset, so forward + BoB can be
+    captured in a HIP graph.  New inputs are copied into the captured buffers before
+    each of several replays (with eager work in between); every replay must equal the
+    eager result on the same inputs bitwise."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    names = ("Q", "K", "V", "dO", "UQ", "UK", "UV")
+    ws = [case(f"graph_n260_h2_bf16_s{s}", 1, 2, 260, 64, "bf16", 40 + s, causal=True)
+          for s in range(3)]
+    U.say("[parity] hip graph capture, 3 replays")
+    inputs = [U.to_device(U.make_inputs(w), w.dtype) for w in ws]
+    static = {k: inputs[0][k].clone() for k in names}
+    tau = ws[0].tau
+
+    def run(t):
+        O, L, D = fb.forward(t["Q"], t["K"], t["V"], t["dO"], tau, True)
+        out = fb.bob(*(t[k] for k in names), O, L, D, tau, True)
+        out.update(O=O, L=L, D=D)
+        return out
+
+    run(static)  # warm-up outside the capture (library load, lazy init)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run(static)
+    torch.cuda.synchronize()
+    for rep, t in enumerate(inputs):
+        eager = run(t)
+        torch.cuda.synchronize()
+        for k in names:
+            static[k].copy_(t[k])
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(captured[k], eager[k]), (rep, k)
