@@ -69,7 +69,8 @@ WORKLOADS = {
 # The pages' isolated-op benchmark setting (FlashBoB notes, experiments table):
 # causal mask, batch 4, 12 heads, bf16, at the table's sequence lengths and head dims.
 for _n, _d, _seed in ((4096, 64, 2001), (8192, 64, 2002), (16384, 64, 2003),
-                      (16384, 128, 2004), (32768, 128, 2005)):
+                      (16384, 128, 2004), (32768, 128, 2005), (65536, 128, 2006),
+                      (262144, 64, 2007)):
     _name = f"pages_causal_b4_h12_n{_n}_d{_d}_bf16"
     WORKLOADS[_name] = Workload(_name, B=4, H=12, N=_n, d=_d, dtype="bf16", seed=_seed,
                                 causal=True, note="pages' benchmark shape (causal, B=4, H=12)")
