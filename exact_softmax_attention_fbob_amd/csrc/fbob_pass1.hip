@@ -16,8 +16,9 @@
 //
 // Schedule: one work-group = NW waves; each wave owns 16 query rows whose Q,
 // tau Q, tau U_Q and dO operand fragments and the fp32 accumulators stay in
-// registers for the whole sweep.  K, V, U_K, U_V tiles of 32 keys are staged
-// through LDS (double-buffered, one barrier per tile).  The four score-shaped
+// registers for the whole sweep.  K, V, U_K, U_V tiles of BC keys (64 by default,
+// processed as 32-key halves) are staged through LDS (double-buffered, one barrier
+// per stage).  The four score-shaped
 // tiles are computed transposed (key index on the MFMA row axis, query row on the
 // column axis): their C registers are directly the B operand of the contractions
 // over keys, whose A operand (K^T, V^T, U_K^T, U_V^T) comes from transposed LDS

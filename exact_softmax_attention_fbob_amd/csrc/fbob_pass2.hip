@@ -16,12 +16,14 @@
 //   dS = P t,   ddP = P u,   dS~ = P (u t + g'),
 // and t, u, g' come straight out of the MFMAs by seeding their accumulators with
 // the row scalars -D, -alpha and -(E + alpha D); tau is folded into the resident
-// K and U_K operands of the F tile.  That leaves five VALU operations plus one exp
-// per score element.
+// K and U_K operands of the F tile (at d = 128, where tau is not a power of two,
+// the operands stay unscaled, the F - alpha accumulator is seeded with
+// -alpha / tau and scaled by tau on the VALU).  That leaves five VALU operations
+// plus one exp per score element.
 //
-// Schedule: one work-group = NW waves; each wave owns 16 key positions whose K,
-// tau K, tau U_K, V, U_V operand fragments and the two fp32 accumulators stay in
-// registers.  Q, dO, U_Q row tiles (kBRs rows) plus the four derived row scalars
+// Schedule: one work-group = NW waves; each wave owns 16 NJ key positions whose
+// K, tau K, tau U_K, V, U_V operand fragments and the two fp32 accumulators stay
+// in registers.  Q, dO, U_Q row tiles (BRS rows) plus the four derived row scalars
 // are staged through LDS (double-buffered).  Scores are computed with the query
 // index on the MFMA row axis, so a lane owns one key and four consecutive rows
 // per block; those C registers are directly the B operand of the contractions
