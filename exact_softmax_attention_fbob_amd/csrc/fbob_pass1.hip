@@ -68,10 +68,15 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bh = logical / n_row_tiles;
-  // Causal rows near the end see the most keys: dispatch them first so the
-  // shortest tiles fill the tail of the grid.
-  const int rt = CAUSAL ? n_row_tiles - 1 - logical % n_row_tiles : logical % n_row_tiles;
+  // Causal (d = 64): a work-group takes row tiles n - 1 - p and p, so every
+  // work-group sweeps the same number of key tiles; heads stay in consecutive
+  // work-groups (their K/V tiles shared in one L2).  At d = 128 the pairing loop
+  // does not fit the register budget: one tile per work-group, the longest
+  // dispatched first.
+  constexpr bool kFold = CAUSAL && D < 128;
+  const int n_units = kFold ? (n_row_tiles + 1) / 2 : n_row_tiles;
+  const int bh = logical / n_units;
+  const int unit = logical % n_units;
   const int b = bh / Hq, h = bh % Hq, hk = h / group;
   const int64_t q_off = (int64_t)bh * N * D;
   const int64_t kv_off = ((int64_t)b * (Hq / group) + hk) * N * D;
@@ -83,317 +88,326 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
                                 reinterpret_cast<const T*>(a.UK) + kv_off,
                                 reinterpret_cast<const T*>(a.UV) + kv_off};
 
-  // ---- resident row operands (B operand of the transposed score tiles) ----
-  const int iw0 = rt * kBR + w * kRW;
-  // tqf / tuqf hold tau Q / tau U_Q, or Q / U_Q unscaled under kTauValu; qf (Q for
-  // the score tile) is a separate copy only under kTauScaled.
-  constexpr bool kQcopy = TM == kTauScaled;
-  F qf[kQcopy ? NI : 1][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
-  float nl2[NI], dv[NI];
+  auto run_tile = [&](const int rt) {
+    // ---- resident row operands (B operand of the transposed score tiles) ----
+    const int iw0 = rt * kBR + w * kRW;
+    // tqf / tuqf hold tau Q / tau U_Q, or Q / U_Q unscaled under kTauValu; qf (Q for
+    // the score tile) is a separate copy only under kTauScaled.
+    constexpr bool kQcopy = TM == kTauScaled;
+    F qf[kQcopy ? NI : 1][kDC], tqf[NI][kDC], tuqf[NI][kDC], dof[NI][kDC];
+    float nl2[NI], dv[NI];
 #pragma unroll
-  for (int ib = 0; ib < NI; ++ib) {
-    const int i = iw0 + 16 * ib + r;
-#pragma unroll
-    for (int dc = 0; dc < kDC; ++dc) {
-      const F q0 = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
-      const F uq0 = global_frag(UQh, i, N, D, 32 * dc + 8 * g);
-      if constexpr (kQcopy) qf[ib][dc] = q0;
-      tqf[ib][dc] = TM == kTauValu ? q0 : scale_frag<T>(q0, tau);
-      tuqf[ib][dc] = TM == kTauValu ? uq0 : scale_frag<T>(uq0, tau);
-      dof[ib][dc] = global_frag(dOh, i, N, D, 32 * dc + 8 * g);
-    }
-    nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
-    dv[ib] = i < N ? a.D[(int64_t)bh * N + i] : 0.f;
-  }
-  // Row sums by MFMA: an operand of ones in rows 0..7 (for alpha) or rows 8..15
-  // (for E') makes C rows 0..7 hold sum_j P F and rows 8..15 sum_j P dP~'.  Lane
-  // (r, g) therefore holds alpha of row r for g < 2 and E' for g >= 2.
-  const F onesA = r < 8 ? ones_frag<T>() : zero_frag<T>();
-  const F onesE = r < 8 ? zero_frag<T>() : ones_frag<T>();
-  // At d = 128 the registers of the two ones operands are worth more than the VALU
-  // adds: there the row sums are lane-local fp32 partial sums (keys 4 g + q of row
-  // r), reduced over the four lanes of a row at the end.
-  constexpr bool kVsum = D >= 128 || NI >= 2;
-  float asum[NI], esum[NI];
-
-  f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
-  f32x4 accAE[NI];
-#pragma unroll
-  for (int ib = 0; ib < NI; ++ib) {
-    accAE[ib] = splat4(0.f);
-    asum[ib] = 0.f;
-    esum[ib] = 0.f;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      accB[ib][db] = splat4(0.f);
-      accX[ib][db] = accB[ib][db];
-      accW[ib][db] = accB[ib][db];
-      accO[ib][db] = accB[ib][db];
-    }
-  }
-  const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
-  // At d = 128 the lane keeps one LDS offset per access pattern (XOR form).
-  const LdsLane<T, D, (D >= 128 || NI >= 2)> rd(r, g);
-
-  int jend = N;
-  if (CAUSAL) jend = min(N, rt * kBR + kBR);
-  const int ntc = (jend + kBC - 1) / kBC;
-
-  // Operand fragments of one 32-key tile for the contractions over keys.
-  struct Frags {
-    F p[NI], ds[NI], pf[NI], pw[NI];
-  };
-
-  // Scores and elementwise work of one 32-key tile, one 16-key block at a time;
-  // the K, V, U_K, U_V fragments of a block serve every row block of the wave.
-  // The bounds / causal test runs only on edge tiles (a wave-uniform branch
-  // around the P values).
-  // `edge_tag` is a bool (runtime test) or std::true_type / std::false_type (the
-  // test resolved at compile time: a separate straight-line copy).
-  auto score_body = [&](const char* Kt, int j0, Frags& fr, auto edge_tag) {
-    const bool edge = edge_tag;
-    const char* Vt = Kt + kTB;
-    const char* UKt = Kt + 2 * kTB;
-    const char* UVt = Kt + 3 * kTB;
-    const auto rx = rd.fresh();
-    // kPipe: the four fragments of (jb, dc) step it + 1 are read while step it's
-    // MFMAs run (two register slots, alternating).
-    constexpr int kSteps = 2 * kDC;
-    F pk[2], pv[2], puk[2], puv[2];
-    auto rowload = [&](int it, int sl) {
-      pk[sl] = rx.row(Kt, it / kDC, it % kDC);
-      pv[sl] = rx.row(Vt, it / kDC, it % kDC);
-      puk[sl] = rx.row(UKt, it / kDC, it % kDC);
-      puv[sl] = rx.row(UVt, it / kDC, it % kDC);
-    };
-    if constexpr (kPipe) {
-      rowload(0, 0);
-      FBOB_SGB(kSgDsRead, 4);
-    }
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      f32x4 s[NI], t[NI], f[NI], gg[NI];
-#pragma unroll
-      for (int ib = 0; ib < NI; ++ib) {
-        s[ib] = splat4(0.f);
-        t[ib] = splat4(-dv[ib]);
-        f[ib] = splat4(0.f);
-        gg[ib] = splat4(0.f);
-      }
-      if constexpr (kPrioScore) FBOB_PRIO_HIGH();
+    for (int ib = 0; ib < NI; ++ib) {
+      const int i = iw0 + 16 * ib + r;
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
-        const int it = jb * kDC + dc, sl = it & 1;
-        F kf, vf, ukf, uvf;
-        if constexpr (kPipe) {
-          if (it + 1 < kSteps) {
-            rowload(it + 1, sl ^ 1);
-            FBOB_SGB(kSgDsRead, 4);
+        const F q0 = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
+        const F uq0 = global_frag(UQh, i, N, D, 32 * dc + 8 * g);
+        if constexpr (kQcopy) qf[ib][dc] = q0;
+        tqf[ib][dc] = TM == kTauValu ? q0 : scale_frag<T>(q0, tau);
+        tuqf[ib][dc] = TM == kTauValu ? uq0 : scale_frag<T>(uq0, tau);
+        dof[ib][dc] = global_frag(dOh, i, N, D, 32 * dc + 8 * g);
+      }
+      nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
+      dv[ib] = i < N ? a.D[(int64_t)bh * N + i] : 0.f;
+    }
+    // Row sums by MFMA: an operand of ones in rows 0..7 (for alpha) or rows 8..15
+    // (for E') makes C rows 0..7 hold sum_j P F and rows 8..15 sum_j P dP~'.  Lane
+    // (r, g) therefore holds alpha of row r for g < 2 and E' for g >= 2.
+    const F onesA = r < 8 ? ones_frag<T>() : zero_frag<T>();
+    const F onesE = r < 8 ? zero_frag<T>() : ones_frag<T>();
+    // At d = 128 the registers of the two ones operands are worth more than the VALU
+    // adds: there the row sums are lane-local fp32 partial sums (keys 4 g + q of row
+    // r), reduced over the four lanes of a row at the end.
+    constexpr bool kVsum = D >= 128 || NI >= 2;
+    float asum[NI], esum[NI];
+
+    f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
+    f32x4 accAE[NI];
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib) {
+      accAE[ib] = splat4(0.f);
+      asum[ib] = 0.f;
+      esum[ib] = 0.f;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        accB[ib][db] = splat4(0.f);
+        accX[ib][db] = accB[ib][db];
+        accW[ib][db] = accB[ib][db];
+        accO[ib][db] = accB[ib][db];
+      }
+    }
+    const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
+    // At d = 128 the lane keeps one LDS offset per access pattern (XOR form).
+    const LdsLane<T, D, (D >= 128 || NI >= 2)> rd(r, g);
+
+    int jend = N;
+    if (CAUSAL) jend = min(N, rt * kBR + kBR);
+    const int ntc = (jend + kBC - 1) / kBC;
+
+    // Operand fragments of one 32-key tile for the contractions over keys.
+    struct Frags {
+      F p[NI], ds[NI], pf[NI], pw[NI];
+    };
+
+    // Scores and elementwise work of one 32-key tile, one 16-key block at a time;
+    // the K, V, U_K, U_V fragments of a block serve every row block of the wave.
+    // The bounds / causal test runs only on edge tiles (a wave-uniform branch
+    // around the P values).
+    // `edge_tag` is a bool (runtime test) or std::true_type / std::false_type (the
+    // test resolved at compile time: a separate straight-line copy).
+    auto score_body = [&](const char* Kt, int j0, Frags& fr, auto edge_tag) {
+      const bool edge = edge_tag;
+      const char* Vt = Kt + kTB;
+      const char* UKt = Kt + 2 * kTB;
+      const char* UVt = Kt + 3 * kTB;
+      const auto rx = rd.fresh();
+      // kPipe: the four fragments of (jb, dc) step it + 1 are read while step it's
+      // MFMAs run (two register slots, alternating).
+      constexpr int kSteps = 2 * kDC;
+      F pk[2], pv[2], puk[2], puv[2];
+      auto rowload = [&](int it, int sl) {
+        pk[sl] = rx.row(Kt, it / kDC, it % kDC);
+        pv[sl] = rx.row(Vt, it / kDC, it % kDC);
+        puk[sl] = rx.row(UKt, it / kDC, it % kDC);
+        puv[sl] = rx.row(UVt, it / kDC, it % kDC);
+      };
+      if constexpr (kPipe) {
+        rowload(0, 0);
+        FBOB_SGB(kSgDsRead, 4);
+      }
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        f32x4 s[NI], t[NI], f[NI], gg[NI];
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib) {
+          s[ib] = splat4(0.f);
+          t[ib] = splat4(-dv[ib]);
+          f[ib] = splat4(0.f);
+          gg[ib] = splat4(0.f);
+        }
+        if constexpr (kPrioScore) FBOB_PRIO_HIGH();
+#pragma unroll
+        for (int dc = 0; dc < kDC; ++dc) {
+          const int it = jb * kDC + dc, sl = it & 1;
+          F kf, vf, ukf, uvf;
+          if constexpr (kPipe) {
+            if (it + 1 < kSteps) {
+              rowload(it + 1, sl ^ 1);
+              FBOB_SGB(kSgDsRead, 4);
+            }
+            kf = pk[sl];
+            vf = pv[sl];
+            ukf = puk[sl];
+            uvf = puv[sl];
+          } else {
+            kf = rx.row(Kt, jb, dc);
+            vf = rx.row(Vt, jb, dc);
+            ukf = rx.row(UKt, jb, dc);
+            uvf = rx.row(UVt, jb, dc);
           }
-          kf = pk[sl];
-          vf = pv[sl];
-          ukf = puk[sl];
-          uvf = puv[sl];
+#pragma unroll
+          for (int ib = 0; ib < NI; ++ib) {
+            s[ib] = E::mma(kf, kQcopy ? qf[kQcopy ? ib : 0][dc] : tqf[ib][dc], s[ib]);
+            f[ib] = E::mma(kf, tuqf[ib][dc], f[ib]);
+            f[ib] = E::mma(ukf, tqf[ib][dc], f[ib]);
+            t[ib] = E::mma(vf, dof[ib][dc], t[ib]);
+            gg[ib] = E::mma(uvf, dof[ib][dc], gg[ib]);
+          }
+          if constexpr (kPipe) FBOB_SGB(kSgMfma, 5 * NI);
+        }
+        if constexpr (kPrioScore) FBOB_PRIO_LOW();
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib) {
+          if constexpr (TM == kTauValu) f[ib] = tau * f[ib];
+          f32x4 p;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[ib][q], c1, nl2[ib]));
+          if (edge) {
+            const int i = iw0 + 16 * ib + r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int j = j0 + 16 * jb + 4 * g + q;
+              if (j >= N || (CAUSAL && j > i)) p[q] = 0.f;
+            }
+          }
+          // elements 4 jb .. 4 jb + 3 of the fragments
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float pf = p[q] * f[ib][q];
+            const float pw = p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]);
+            fr.p[ib][4 * jb + q] = (T)p[q];
+            fr.ds[ib][4 * jb + q] = (T)(p[q] * t[ib][q]);
+            fr.pf[ib][4 * jb + q] = (T)pf;
+            fr.pw[ib][4 * jb + q] = (T)pw;
+            if constexpr (kVsum) {
+              asum[ib] += pf;
+              esum[ib] += pw;
+            }
+          }
+        }
+      }
+    };
+    // Under kPipe the bounds / causal test is compiled into a separate copy of the
+    // tile body that only edge tiles take, so the pinned schedule spans one
+    // straight-line region; otherwise it is a wave-uniform branch inside the body.
+    auto score_phase = [&](const char* Kt, int j0, Frags& fr) {
+      const bool edge = (j0 + 32 > N) || (CAUSAL && j0 + 31 > iw0);
+      if constexpr (kPipe) {
+        if (edge) score_body(Kt, j0, fr, std::true_type{});
+        else score_body(Kt, j0, fr, std::false_type{});
+      } else {
+        score_body(Kt, j0, fr, edge);
+      }
+    };
+
+    // Contractions over the tile's keys (transposed outputs) and the row sums.
+    auto output_phase = [&](const char* Kt, const Frags& fr) {
+      const char* Vt = Kt + kTB;
+      const char* UKt = Kt + 2 * kTB;
+      const char* UVt = Kt + 3 * kTB;
+      if constexpr (FENCE) FBOB_SCHED_FENCE();
+      if constexpr (kPrioOut) FBOB_PRIO_HIGH();
+      const auto rx = rd.fresh();
+      if constexpr (!kVsum) {
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib) {
+          accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
+          accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
+        }
+        if constexpr (kPipe) FBOB_SGB(kSgMfma, 2 * NI);
+      }
+      // kPipe: the transposed fragments of column block db + 1 are read while
+      // block db's MFMAs run (two register slots; each read is two instructions).
+      F tk[2], tuk[2], tv[2], tuv[2];
+      auto trload = [&](int db, int sl) {
+        tk[sl] = rx.tr(Kt, db);
+        tuk[sl] = rx.tr(UKt, db);
+        tv[sl] = rx.tr(Vt, db);
+        tuv[sl] = rx.tr(UVt, db);
+      };
+      if constexpr (kPipe) {
+        trload(0, 0);
+        FBOB_SGB(kSgDsRead, 8);
+      }
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        if constexpr (FENCE) FBOB_SCHED_FENCE();
+        F kt, ukt, vt, uvt;
+        if constexpr (kPipe) {
+          const int sl = db & 1;
+          if (db + 1 < kDB) {
+            trload(db + 1, sl ^ 1);
+            FBOB_SGB(kSgDsRead, 8);
+          }
+          kt = tk[sl];
+          ukt = tuk[sl];
+          vt = tv[sl];
+          uvt = tuv[sl];
         } else {
-          kf = rx.row(Kt, jb, dc);
-          vf = rx.row(Vt, jb, dc);
-          ukf = rx.row(UKt, jb, dc);
-          uvf = rx.row(UVt, jb, dc);
+          kt = rx.tr(Kt, db);
+          ukt = rx.tr(UKt, db);
+          vt = rx.tr(Vt, db);
+          uvt = rx.tr(UVt, db);
         }
 #pragma unroll
         for (int ib = 0; ib < NI; ++ib) {
-          s[ib] = E::mma(kf, kQcopy ? qf[kQcopy ? ib : 0][dc] : tqf[ib][dc], s[ib]);
-          f[ib] = E::mma(kf, tuqf[ib][dc], f[ib]);
-          f[ib] = E::mma(ukf, tqf[ib][dc], f[ib]);
-          t[ib] = E::mma(vf, dof[ib][dc], t[ib]);
-          gg[ib] = E::mma(uvf, dof[ib][dc], gg[ib]);
+          accB[ib][db] = E::mma(kt, fr.p[ib], accB[ib][db]);
+          accX[ib][db] = E::mma(kt, fr.ds[ib], accX[ib][db]);
+          accW[ib][db] = E::mma(kt, fr.pw[ib], accW[ib][db]);
+          accW[ib][db] = E::mma(ukt, fr.ds[ib], accW[ib][db]);
+          accO[ib][db] = E::mma(vt, fr.pf[ib], accO[ib][db]);
+          accO[ib][db] = E::mma(uvt, fr.p[ib], accO[ib][db]);
         }
-        if constexpr (kPipe) FBOB_SGB(kSgMfma, 5 * NI);
+        if constexpr (kPipe) FBOB_SGB(kSgMfma, 6 * NI);
       }
-      if constexpr (kPrioScore) FBOB_PRIO_LOW();
-#pragma unroll
-      for (int ib = 0; ib < NI; ++ib) {
-        if constexpr (TM == kTauValu) f[ib] = tau * f[ib];
-        f32x4 p;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[ib][q], c1, nl2[ib]));
-        if (edge) {
-          const int i = iw0 + 16 * ib + r;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int j = j0 + 16 * jb + 4 * g + q;
-            if (j >= N || (CAUSAL && j > i)) p[q] = 0.f;
-          }
-        }
-        // elements 4 jb .. 4 jb + 3 of the fragments
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float pf = p[q] * f[ib][q];
-          const float pw = p[q] * __builtin_fmaf(f[ib][q], t[ib][q], gg[ib][q]);
-          fr.p[ib][4 * jb + q] = (T)p[q];
-          fr.ds[ib][4 * jb + q] = (T)(p[q] * t[ib][q]);
-          fr.pf[ib][4 * jb + q] = (T)pf;
-          fr.pw[ib][4 * jb + q] = (T)pw;
-          if constexpr (kVsum) {
-            asum[ib] += pf;
-            esum[ib] += pw;
-          }
-        }
-      }
-    }
-  };
-  // Under kPipe the bounds / causal test is compiled into a separate copy of the
-  // tile body that only edge tiles take, so the pinned schedule spans one
-  // straight-line region; otherwise it is a wave-uniform branch inside the body.
-  auto score_phase = [&](const char* Kt, int j0, Frags& fr) {
-    const bool edge = (j0 + 32 > N) || (CAUSAL && j0 + 31 > iw0);
-    if constexpr (kPipe) {
-      if (edge) score_body(Kt, j0, fr, std::true_type{});
-      else score_body(Kt, j0, fr, std::false_type{});
-    } else {
-      score_body(Kt, j0, fr, edge);
-    }
-  };
-
-  // Contractions over the tile's keys (transposed outputs) and the row sums.
-  auto output_phase = [&](const char* Kt, const Frags& fr) {
-    const char* Vt = Kt + kTB;
-    const char* UKt = Kt + 2 * kTB;
-    const char* UVt = Kt + 3 * kTB;
-    if constexpr (FENCE) FBOB_SCHED_FENCE();
-    if constexpr (kPrioOut) FBOB_PRIO_HIGH();
-    const auto rx = rd.fresh();
-    if constexpr (!kVsum) {
-#pragma unroll
-      for (int ib = 0; ib < NI; ++ib) {
-        accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
-        accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
-      }
-      if constexpr (kPipe) FBOB_SGB(kSgMfma, 2 * NI);
-    }
-    // kPipe: the transposed fragments of column block db + 1 are read while
-    // block db's MFMAs run (two register slots; each read is two instructions).
-    F tk[2], tuk[2], tv[2], tuv[2];
-    auto trload = [&](int db, int sl) {
-      tk[sl] = rx.tr(Kt, db);
-      tuk[sl] = rx.tr(UKt, db);
-      tv[sl] = rx.tr(Vt, db);
-      tuv[sl] = rx.tr(UVt, db);
+      if constexpr (kPrioOut) FBOB_PRIO_LOW();
     };
-    if constexpr (kPipe) {
-      trload(0, 0);
-      FBOB_SGB(kSgDsRead, 8);
-    }
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      if constexpr (FENCE) FBOB_SCHED_FENCE();
-      F kt, ukt, vt, uvt;
-      if constexpr (kPipe) {
-        const int sl = db & 1;
-        if (db + 1 < kDB) {
-          trload(db + 1, sl ^ 1);
-          FBOB_SGB(kSgDsRead, 8);
-        }
-        kt = tk[sl];
-        ukt = tuk[sl];
-        vt = tv[sl];
-        uvt = tuv[sl];
-      } else {
-        kt = rx.tr(Kt, db);
-        ukt = rx.tr(UKt, db);
-        vt = rx.tr(Vt, db);
-        uvt = rx.tr(UVt, db);
-      }
-#pragma unroll
-      for (int ib = 0; ib < NI; ++ib) {
-        accB[ib][db] = E::mma(kt, fr.p[ib], accB[ib][db]);
-        accX[ib][db] = E::mma(kt, fr.ds[ib], accX[ib][db]);
-        accW[ib][db] = E::mma(kt, fr.pw[ib], accW[ib][db]);
-        accW[ib][db] = E::mma(ukt, fr.ds[ib], accW[ib][db]);
-        accO[ib][db] = E::mma(vt, fr.pf[ib], accO[ib][db]);
-        accO[ib][db] = E::mma(uvt, fr.p[ib], accO[ib][db]);
-      }
-      if constexpr (kPipe) FBOB_SGB(kSgMfma, 6 * NI);
-    }
-    if constexpr (kPrioOut) FBOB_PRIO_LOW();
-  };
 
-  // Staging: registers + ds_write (MultiStager) or direct global -> LDS.
-  using RegStager = MultiStager<T, D, kBC, 4, kThreads>;
-  using DirStager = DirectStager<T, D, kBC, 4, NW>;
-  typename std::conditional<DIRECT, DirStager, RegStager>::type st;
-  auto stage_init = [&]() {
-    if constexpr (DIRECT) st.init(kv_bases, w, lane);
-    else st.init(kv_bases, tid);
-  };
-  // Issue the loads of the tile at key j0 (into `buf` when DIRECT).
-  auto stage_load = [&](char* buf, int j0) {
-    if constexpr (DIRECT) st.load(buf, j0, N);
-    else st.load(j0, N);
-  };
-  // Make the staged tile visible in `buf` (the barrier follows).
-  auto stage_commit = [&](char* buf) {
-    if constexpr (DIRECT) wait_all_memory();
-    else st.store(buf);
-  };
-  stage_init();
-  stage_load(lds[0], 0);
-  stage_commit(lds[0]);
-  __syncthreads();
-
-  auto active_tile = [&](int t) { return !CAUSAL || t * kBC <= iw0 + kRW - 1; };
-  // Both 32-key halves of a stage (BC = 64) or the single one (BC = 32).
-  auto compute_stage = [&](const char* cur, int j0) {
-#pragma unroll
-    for (int hs = 0; hs < kBC / 32; ++hs) {
-      const int js = j0 + 32 * hs;
-      if (!CAUSAL || js <= iw0 + kRW - 1) {
-        Frags fr;
-        score_phase(cur + 32 * hs * Tile<T, D>::kRowBytes, js, fr);
-        output_phase(cur + 32 * hs * Tile<T, D>::kRowBytes, fr);
-      }
-    }
-  };
-
-  // One pipeline step: prefetch tile t+1, compute tile t from `cur`, publish
-  // tile t+1 in `nxt`, barrier.  Unrolled by two so that both LDS buffers are
-  // compile-time addresses.
-  auto step = [&](int t, char* cur, char* nxt) {
-    const int j0 = t * kBC;
-    const bool more = t + 1 < ntc;
-    if (more) stage_load(nxt, j0 + kBC);
-    if (active_tile(t)) compute_stage(cur, j0);
-    if (more) stage_commit(nxt);
+    // Staging: registers + ds_write (MultiStager) or direct global -> LDS.
+    using RegStager = MultiStager<T, D, kBC, 4, kThreads>;
+    using DirStager = DirectStager<T, D, kBC, 4, NW>;
+    typename std::conditional<DIRECT, DirStager, RegStager>::type st;
+    auto stage_init = [&]() {
+      if constexpr (DIRECT) st.init(kv_bases, w, lane);
+      else st.init(kv_bases, tid);
+    };
+    // Issue the loads of the tile at key j0 (into `buf` when DIRECT).
+    auto stage_load = [&](char* buf, int j0) {
+      if constexpr (DIRECT) st.load(buf, j0, N);
+      else st.load(j0, N);
+    };
+    // Make the staged tile visible in `buf` (the barrier follows).
+    auto stage_commit = [&](char* buf) {
+      if constexpr (DIRECT) wait_all_memory();
+      else st.store(buf);
+    };
+    stage_init();
+    stage_load(lds[0], 0);
+    stage_commit(lds[0]);
     __syncthreads();
-  };
-#pragma unroll 1
-  for (int t = 0; t < ntc; t += 2) {
-    step(t, lds[0], lds[1]);
-    if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
-  }
 
-  // ---- row correction and the single write of each row output ----
+    auto active_tile = [&](int t) { return !CAUSAL || t * kBC <= iw0 + kRW - 1; };
+    // Both 32-key halves of a stage (BC = 64) or the single one (BC = 32).
+    auto compute_stage = [&](const char* cur, int j0) {
 #pragma unroll
-  for (int ib = 0; ib < NI; ++ib) {
-    const int i = iw0 + 16 * ib + r;
-    // F carries tau through the scaled resident operands.
-    const float al = kVsum ? group_sum(asum[ib]) : __shfl(accAE[ib][0], r);
-    const float edeg = kVsum ? group_sum(esum[ib]) : __shfl(accAE[ib][0], 32 + r);
-    if (i < N) {
-      const int64_t ro = q_off + (int64_t)i * D;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const int d0 = 16 * db + 4 * g;
-        const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro + d0);
-        *reinterpret_cast<f32x4*>(a.ddOt + ro + d0) = accO[ib][db] - al * o;
-        *reinterpret_cast<f32x4*>(a.dQt + ro + d0) =
-            tau * (accW[ib][db] - al * accX[ib][db] - edeg * accB[ib][db]);
+      for (int hs = 0; hs < kBC / 32; ++hs) {
+        const int js = j0 + 32 * hs;
+        if (!CAUSAL || js <= iw0 + kRW - 1) {
+          Frags fr;
+          score_phase(cur + 32 * hs * Tile<T, D>::kRowBytes, js, fr);
+          output_phase(cur + 32 * hs * Tile<T, D>::kRowBytes, fr);
+        }
       }
-      if (g == 0) {
-        a.alpha[(int64_t)bh * N + i] = al;
-        a.E[(int64_t)bh * N + i] = edeg - al * dv[ib];
+    };
+
+    // One pipeline step: prefetch tile t+1, compute tile t from `cur`, publish
+    // tile t+1 in `nxt`, barrier.  Unrolled by two so that both LDS buffers are
+    // compile-time addresses.
+    auto step = [&](int t, char* cur, char* nxt) {
+      const int j0 = t * kBC;
+      const bool more = t + 1 < ntc;
+      if (more) stage_load(nxt, j0 + kBC);
+      if (active_tile(t)) compute_stage(cur, j0);
+      if (more) stage_commit(nxt);
+      __syncthreads();
+    };
+#pragma unroll 1
+    for (int t = 0; t < ntc; t += 2) {
+      step(t, lds[0], lds[1]);
+      if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
+    }
+
+    // ---- row correction and the single write of each row output ----
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib) {
+      const int i = iw0 + 16 * ib + r;
+      // F carries tau through the scaled resident operands.
+      const float al = kVsum ? group_sum(asum[ib]) : __shfl(accAE[ib][0], r);
+      const float edeg = kVsum ? group_sum(esum[ib]) : __shfl(accAE[ib][0], 32 + r);
+      if (i < N) {
+        const int64_t ro = q_off + (int64_t)i * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int d0 = 16 * db + 4 * g;
+          const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro + d0);
+          *reinterpret_cast<f32x4*>(a.ddOt + ro + d0) = accO[ib][db] - al * o;
+          *reinterpret_cast<f32x4*>(a.dQt + ro + d0) =
+              tau * (accW[ib][db] - al * accX[ib][db] - edeg * accB[ib][db]);
+        }
+        if (g == 0) {
+          a.alpha[(int64_t)bh * N + i] = al;
+          a.E[(int64_t)bh * N + i] = edeg - al * dv[ib];
+        }
       }
     }
+  };
+  if constexpr (kFold) {
+    const int n_tiles_here = unit != n_row_tiles - 1 - unit ? 2 : 1;
+#pragma unroll 1
+    for (int tile = 0; tile < n_tiles_here; ++tile) run_tile(tile == 0 ? n_row_tiles - 1 - unit : unit);
+  } else {
+    run_tile(CAUSAL ? n_row_tiles - 1 - unit : unit);
   }
 }
 
@@ -401,7 +415,9 @@ template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC = 32, boo
 hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
-  const int total = n_row_tiles * p.B * p.Hq;
+  // causal d = 64: row tiles paired per work-group (see the kernel)
+  const int n_units = p.causal && D < 128 ? (n_row_tiles + 1) / 2 : n_row_tiles;
+  const int total = n_units * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
     hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,

@@ -63,7 +63,12 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bhk = logical / n_col_tiles, ct = logical % n_col_tiles;
+  // Causal (d = 64): a work-group takes column tiles p and n - 1 - p, so every
+  // work-group sweeps the same number of row chunks (the first has the most);
+  // key/value heads stay in consecutive work-groups.
+  constexpr bool kFold = CAUSAL && D < 128;
+  const int n_units = kFold ? (n_col_tiles + 1) / 2 : n_col_tiles;
+  const int bhk = logical / n_units, unit = logical % n_units;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int Hq = Hkv * group;
   const int64_t kv_off = (int64_t)bhk * N * D;
@@ -72,197 +77,202 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   const T* UKh = reinterpret_cast<const T*>(a.UK) + kv_off;
   const T* UVh = reinterpret_cast<const T*>(a.UV) + kv_off;
 
-  const int jw0 = ct * kBCw + w * kCW;
-  // tkf / tukf hold tau K / tau U_K, or K / U_K unscaled under kTauValu; kf (K for
-  // the score tile) is a separate copy only under kTauScaled.
-  constexpr bool kKcopy = TM == kTauScaled;
-  F kf[kKcopy ? NJ : 1][kDC], tkf[NJ][kDC], tukf[NJ][kDC], vf[NJ][kDC], uvf[NJ][kDC];
+  const int n_tiles_here = kFold && unit != n_col_tiles - 1 - unit ? 2 : 1;
+#pragma unroll 1
+  for (int tile = 0; tile < n_tiles_here; ++tile) {
+    const int ct = tile == 0 ? unit : n_col_tiles - 1 - unit;
+    const int jw0 = ct * kBCw + w * kCW;
+    // tkf / tukf hold tau K / tau U_K, or K / U_K unscaled under kTauValu; kf (K for
+    // the score tile) is a separate copy only under kTauScaled.
+    constexpr bool kKcopy = TM == kTauScaled;
+    F kf[kKcopy ? NJ : 1][kDC], tkf[NJ][kDC], tukf[NJ][kDC], vf[NJ][kDC], uvf[NJ][kDC];
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
-#pragma unroll
-    for (int dc = 0; dc < kDC; ++dc) {
-      const int j = jw0 + 16 * jb + r, col = 32 * dc + 8 * g;
-      const F k0 = global_frag(Kh, j, N, D, col);
-      const F uk0 = global_frag(UKh, j, N, D, col);
-      if constexpr (kKcopy) kf[jb][dc] = k0;
-      tkf[jb][dc] = TM == kTauValu ? k0 : scale_frag<T>(k0, tau);
-      tukf[jb][dc] = TM == kTauValu ? uk0 : scale_frag<T>(uk0, tau);
-      vf[jb][dc] = global_frag(Vh, j, N, D, col);
-      uvf[jb][dc] = global_frag(UVh, j, N, D, col);
-    }
-
-  f32x4 accK[NJ][kDB], accV[NJ][kDB];
-#pragma unroll
-  for (int jb = 0; jb < NJ; ++jb)
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      accK[jb][db] = splat4(0.f);
-      accV[jb][db] = accK[jb][db];
-    }
-  const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
-  // Under kTauValu the F - alpha tile accumulates F / tau - alpha / tau and is scaled
-  // by tau afterwards, so its seed is -alpha / tau.
-  const float inv_tau = TM == kTauValu ? 1.f / tau : 1.f;
-  const LdsLane<T, D> rd(r, g);
-
-  // Row steps: (query head of the group, row chunk); causal rows start at the
-  // work-group's first key.
-  const int i_begin = CAUSAL ? (ct * kBCw / BRS) * BRS : 0;
-  const int nrc = (N - i_begin + BRS - 1) / BRS;
-  const int nsteps = nrc * group;
-
-  const int64_t q_head = (int64_t)N * D * (int64_t)sizeof(T);  // bytes per query head
-  const int64_t q0 = ((int64_t)b * Hq + (int64_t)hk * group) * N * D;
-  const T* const q_bases[3] = {reinterpret_cast<const T*>(a.Q) + q0,
-                               reinterpret_cast<const T*>(a.dO) + q0,
-                               reinterpret_cast<const T*>(a.UQ) + q0};
-  // Q, dO, U_Q tiles: registers + ds_write (MultiStager) or direct global -> LDS.
-  using RegStager = MultiStager<T, D, BRS, 3, kThreads>;
-  using DirStager = DirectStager<T, D, BRS, 3, NW>;
-  typename std::conditional<DIRECT, DirStager, RegStager>::type st;
-  if constexpr (DIRECT) st.init(q_bases, w, lane);
-  else st.init(q_bases, tid);
-  // Row scalars: thread tid < BRS stages row tid of the chunk.
-  const int64_t s0 = ((int64_t)b * Hq + (int64_t)hk * group) * N;
-  f32x4 scal = splat4(0.f);
-  // Issue the loads of step `step` (tiles go straight into `buf` when DIRECT).
-  auto load_step = [&](int step, char* buf) {
-    const int hq = step / nrc;
-    const int i0 = i_begin + (step % nrc) * BRS;
-    if constexpr (DIRECT) st.load(buf, i0, N, hq * q_head);
-    else st.load(i0, N, hq * q_head);
-    if (tid < BRS) {
-      const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
-      const float L = a.L[ri], Dv = a.D[ri], al = a.alpha[ri], Ev = a.E[ri];
-      scal = f32x4{-L * kLog2e, -Dv, -al * inv_tau, -(Ev + al * Dv)};
-    }
-  };
-  auto store_step = [&](char* buf) {
-    if constexpr (DIRECT) wait_all_memory();
-    else st.store(buf);
-    if (tid < BRS) {
-      float* sp = reinterpret_cast<float*>(buf + 3 * kTB);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) sp[m * BRS + tid] = scal[m];
-    }
-  };
-
-  // 32 rows of a staged tile (sub-chunk sc): scores, elementwise, contractions.
-  auto chunk = [&](const char* buf, int i0, int sc) {
-    const char* Qt = buf;
-    const char* dOt = buf + kTB;
-    const char* UQt = buf + 2 * kTB;
-    const float* sp = reinterpret_cast<const float*>(buf + 3 * kTB);
-    const int ic = i0 + 32 * sc;
-    const bool edge = (ic + 32 > N) || (CAUSAL && ic < jw0 + kCW - 1);
-    F dsB[NJ], ddpB[NJ], dstB[NJ];  // filled half by half: elements 4 ib .. 4 ib + 3
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      const int rr = 32 * sc + 16 * ib + 4 * g;  // first of this lane's 4 rows in the tile
-      const f32x4 nL = *reinterpret_cast<const f32x4*>(sp + rr);
-      const f32x4 nD = *reinterpret_cast<const f32x4*>(sp + BRS + rr);
-      const f32x4 nA = *reinterpret_cast<const f32x4*>(sp + 2 * BRS + rr);
-      const f32x4 nG = *reinterpret_cast<const f32x4*>(sp + 3 * BRS + rr);
-      f32x4 s[NJ], t[NJ], u[NJ], gp[NJ];
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        s[jb] = splat4(0.f);
-        t[jb] = nD;
-        u[jb] = nA;
-        gp[jb] = nG;
-      }
-      if constexpr (kPrioScore) FBOB_PRIO_HIGH();
+    for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
       for (int dc = 0; dc < kDC; ++dc) {
-        const F qa = rd.row(Qt, 2 * sc + ib, dc);
-        const F doa = rd.row(dOt, 2 * sc + ib, dc);
-        const F uqa = rd.row(UQt, 2 * sc + ib, dc);
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) {
-          s[jb] = E::mma(qa, kKcopy ? kf[kKcopy ? jb : 0][dc] : tkf[jb][dc], s[jb]);
-          u[jb] = E::mma(uqa, tkf[jb][dc], u[jb]);
-          u[jb] = E::mma(qa, tukf[jb][dc], u[jb]);
-          t[jb] = E::mma(doa, vf[jb][dc], t[jb]);
-          gp[jb] = E::mma(doa, uvf[jb][dc], gp[jb]);
-        }
+        const int j = jw0 + 16 * jb + r, col = 32 * dc + 8 * g;
+        const F k0 = global_frag(Kh, j, N, D, col);
+        const F uk0 = global_frag(UKh, j, N, D, col);
+        if constexpr (kKcopy) kf[jb][dc] = k0;
+        tkf[jb][dc] = TM == kTauValu ? k0 : scale_frag<T>(k0, tau);
+        tukf[jb][dc] = TM == kTauValu ? uk0 : scale_frag<T>(uk0, tau);
+        vf[jb][dc] = global_frag(Vh, j, N, D, col);
+        uvf[jb][dc] = global_frag(UVh, j, N, D, col);
       }
-      if constexpr (kPrioScore) FBOB_PRIO_LOW();
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        if constexpr (TM == kTauValu) u[jb] = tau * u[jb];
-        f32x4 p;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[jb][q], c1, nL[q]));
-        if (edge) {
-          const int j = jw0 + 16 * jb + r;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = ic + 16 * ib + 4 * g + q;
-            if (i >= N || (CAUSAL && j > i)) p[q] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          dsB[jb][4 * ib + q] = (T)(p[q] * t[jb][q]);
-          ddpB[jb][4 * ib + q] = (T)(p[q] * u[jb][q]);
-          dstB[jb][4 * ib + q] = (T)(p[q] * __builtin_fmaf(u[jb][q], t[jb][q], gp[jb][q]));
-        }
-      }
-    }
-    if constexpr (FENCE) FBOB_SCHED_FENCE();
-    if constexpr (kPrioOut) FBOB_PRIO_HIGH();
-    const char* Qs = Qt + 32 * sc * Tile<T, D>::kRowBytes;
-    const char* dOs = dOt + 32 * sc * Tile<T, D>::kRowBytes;
-    const char* UQs = UQt + 32 * sc * Tile<T, D>::kRowBytes;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      if constexpr (FENCE) FBOB_SCHED_FENCE();
-      const F qt = rd.tr(Qs, db);
-      const F uqt = rd.tr(UQs, db);
-      const F dot = rd.tr(dOs, db);
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        accK[jb][db] = E::mma(qt, dstB[jb], accK[jb][db]);
-        accK[jb][db] = E::mma(uqt, dsB[jb], accK[jb][db]);
-        accV[jb][db] = E::mma(dot, ddpB[jb], accV[jb][db]);
-      }
-    }
-    if constexpr (kPrioOut) FBOB_PRIO_LOW();
-  };
 
-  load_step(0, lds[0]);
-  store_step(lds[0]);
-  __syncthreads();
-
-  auto step = [&](int t, char* cur, char* nxt) {
-    const int i0 = i_begin + (t % nrc) * BRS;
-    const bool more = t + 1 < nsteps;
-    if (more) load_step(t + 1, nxt);
+    f32x4 accK[NJ][kDB], accV[NJ][kDB];
 #pragma unroll
-    for (int sc = 0; sc < BRS / 32; ++sc) {
-      const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
-      if (active) chunk(cur, i0, sc);
-    }
-    if (more) store_step(nxt);
-    __syncthreads();
-  };
-#pragma unroll 1
-  for (int t = 0; t < nsteps; t += 2) {
-    step(t, lds[0], lds[1]);
-    if (t + 1 < nsteps) step(t + 1, lds[1], lds[0]);
-  }
-
-  // ---- single exclusive write of dK~ and dV~ ----
-#pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) {
-    const int j = jw0 + 16 * jb + r;
-    if (j < N) {
-      const int64_t ro = kv_off + (int64_t)j * D;
+    for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const int d0 = 16 * db + 4 * g;
-        *reinterpret_cast<f32x4*>(a.dKt + ro + d0) = tau * accK[jb][db];
-        *reinterpret_cast<f32x4*>(a.dVt + ro + d0) = accV[jb][db];
+        accK[jb][db] = splat4(0.f);
+        accV[jb][db] = accK[jb][db];
+      }
+    const float c1 = TM == kTauPow2 ? kLog2e : tau * kLog2e;
+    // Under kTauValu the F - alpha tile accumulates F / tau - alpha / tau and is scaled
+    // by tau afterwards, so its seed is -alpha / tau.
+    const float inv_tau = TM == kTauValu ? 1.f / tau : 1.f;
+    const LdsLane<T, D> rd(r, g);
+
+    // Row steps: (query head of the group, row chunk); causal rows start at the
+    // work-group's first key.
+    const int i_begin = CAUSAL ? (ct * kBCw / BRS) * BRS : 0;
+    const int nrc = (N - i_begin + BRS - 1) / BRS;
+    const int nsteps = nrc * group;
+
+    const int64_t q_head = (int64_t)N * D * (int64_t)sizeof(T);  // bytes per query head
+    const int64_t q0 = ((int64_t)b * Hq + (int64_t)hk * group) * N * D;
+    const T* const q_bases[3] = {reinterpret_cast<const T*>(a.Q) + q0,
+                                 reinterpret_cast<const T*>(a.dO) + q0,
+                                 reinterpret_cast<const T*>(a.UQ) + q0};
+    // Q, dO, U_Q tiles: registers + ds_write (MultiStager) or direct global -> LDS.
+    using RegStager = MultiStager<T, D, BRS, 3, kThreads>;
+    using DirStager = DirectStager<T, D, BRS, 3, NW>;
+    typename std::conditional<DIRECT, DirStager, RegStager>::type st;
+    if constexpr (DIRECT) st.init(q_bases, w, lane);
+    else st.init(q_bases, tid);
+    // Row scalars: thread tid < BRS stages row tid of the chunk.
+    const int64_t s0 = ((int64_t)b * Hq + (int64_t)hk * group) * N;
+    f32x4 scal = splat4(0.f);
+    // Issue the loads of step `step` (tiles go straight into `buf` when DIRECT).
+    auto load_step = [&](int step, char* buf) {
+      const int hq = step / nrc;
+      const int i0 = i_begin + (step % nrc) * BRS;
+      if constexpr (DIRECT) st.load(buf, i0, N, hq * q_head);
+      else st.load(i0, N, hq * q_head);
+      if (tid < BRS) {
+        const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
+        const float L = a.L[ri], Dv = a.D[ri], al = a.alpha[ri], Ev = a.E[ri];
+        scal = f32x4{-L * kLog2e, -Dv, -al * inv_tau, -(Ev + al * Dv)};
+      }
+    };
+    auto store_step = [&](char* buf) {
+      if constexpr (DIRECT) wait_all_memory();
+      else st.store(buf);
+      if (tid < BRS) {
+        float* sp = reinterpret_cast<float*>(buf + 3 * kTB);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sp[m * BRS + tid] = scal[m];
+      }
+    };
+
+    // 32 rows of a staged tile (sub-chunk sc): scores, elementwise, contractions.
+    auto chunk = [&](const char* buf, int i0, int sc) {
+      const char* Qt = buf;
+      const char* dOt = buf + kTB;
+      const char* UQt = buf + 2 * kTB;
+      const float* sp = reinterpret_cast<const float*>(buf + 3 * kTB);
+      const int ic = i0 + 32 * sc;
+      const bool edge = (ic + 32 > N) || (CAUSAL && ic < jw0 + kCW - 1);
+      F dsB[NJ], ddpB[NJ], dstB[NJ];  // filled half by half: elements 4 ib .. 4 ib + 3
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const int rr = 32 * sc + 16 * ib + 4 * g;  // first of this lane's 4 rows in the tile
+        const f32x4 nL = *reinterpret_cast<const f32x4*>(sp + rr);
+        const f32x4 nD = *reinterpret_cast<const f32x4*>(sp + BRS + rr);
+        const f32x4 nA = *reinterpret_cast<const f32x4*>(sp + 2 * BRS + rr);
+        const f32x4 nG = *reinterpret_cast<const f32x4*>(sp + 3 * BRS + rr);
+        f32x4 s[NJ], t[NJ], u[NJ], gp[NJ];
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+          s[jb] = splat4(0.f);
+          t[jb] = nD;
+          u[jb] = nA;
+          gp[jb] = nG;
+        }
+        if constexpr (kPrioScore) FBOB_PRIO_HIGH();
+#pragma unroll
+        for (int dc = 0; dc < kDC; ++dc) {
+          const F qa = rd.row(Qt, 2 * sc + ib, dc);
+          const F doa = rd.row(dOt, 2 * sc + ib, dc);
+          const F uqa = rd.row(UQt, 2 * sc + ib, dc);
+#pragma unroll
+          for (int jb = 0; jb < NJ; ++jb) {
+            s[jb] = E::mma(qa, kKcopy ? kf[kKcopy ? jb : 0][dc] : tkf[jb][dc], s[jb]);
+            u[jb] = E::mma(uqa, tkf[jb][dc], u[jb]);
+            u[jb] = E::mma(qa, tukf[jb][dc], u[jb]);
+            t[jb] = E::mma(doa, vf[jb][dc], t[jb]);
+            gp[jb] = E::mma(doa, uvf[jb][dc], gp[jb]);
+          }
+        }
+        if constexpr (kPrioScore) FBOB_PRIO_LOW();
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+          if constexpr (TM == kTauValu) u[jb] = tau * u[jb];
+          f32x4 p;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) p[q] = fast_exp2(__builtin_fmaf(s[jb][q], c1, nL[q]));
+          if (edge) {
+            const int j = jw0 + 16 * jb + r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int i = ic + 16 * ib + 4 * g + q;
+              if (i >= N || (CAUSAL && j > i)) p[q] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            dsB[jb][4 * ib + q] = (T)(p[q] * t[jb][q]);
+            ddpB[jb][4 * ib + q] = (T)(p[q] * u[jb][q]);
+            dstB[jb][4 * ib + q] = (T)(p[q] * __builtin_fmaf(u[jb][q], t[jb][q], gp[jb][q]));
+          }
+        }
+      }
+      if constexpr (FENCE) FBOB_SCHED_FENCE();
+      if constexpr (kPrioOut) FBOB_PRIO_HIGH();
+      const char* Qs = Qt + 32 * sc * Tile<T, D>::kRowBytes;
+      const char* dOs = dOt + 32 * sc * Tile<T, D>::kRowBytes;
+      const char* UQs = UQt + 32 * sc * Tile<T, D>::kRowBytes;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        if constexpr (FENCE) FBOB_SCHED_FENCE();
+        const F qt = rd.tr(Qs, db);
+        const F uqt = rd.tr(UQs, db);
+        const F dot = rd.tr(dOs, db);
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+          accK[jb][db] = E::mma(qt, dstB[jb], accK[jb][db]);
+          accK[jb][db] = E::mma(uqt, dsB[jb], accK[jb][db]);
+          accV[jb][db] = E::mma(dot, ddpB[jb], accV[jb][db]);
+        }
+      }
+      if constexpr (kPrioOut) FBOB_PRIO_LOW();
+    };
+
+    load_step(0, lds[0]);
+    store_step(lds[0]);
+    __syncthreads();
+
+    auto step = [&](int t, char* cur, char* nxt) {
+      const int i0 = i_begin + (t % nrc) * BRS;
+      const bool more = t + 1 < nsteps;
+      if (more) load_step(t + 1, nxt);
+#pragma unroll
+      for (int sc = 0; sc < BRS / 32; ++sc) {
+        const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
+        if (active) chunk(cur, i0, sc);
+      }
+      if (more) store_step(nxt);
+      __syncthreads();
+    };
+#pragma unroll 1
+    for (int t = 0; t < nsteps; t += 2) {
+      step(t, lds[0], lds[1]);
+      if (t + 1 < nsteps) step(t + 1, lds[1], lds[0]);
+    }
+
+    // ---- single exclusive write of dK~ and dV~ ----
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+      const int j = jw0 + 16 * jb + r;
+      if (j < N) {
+        const int64_t ro = kv_off + (int64_t)j * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int d0 = 16 * db + 4 * g;
+          *reinterpret_cast<f32x4*>(a.dKt + ro + d0) = tau * accK[jb][db];
+          *reinterpret_cast<f32x4*>(a.dVt + ro + d0) = accV[jb][db];
+        }
       }
     }
   }
@@ -272,7 +282,9 @@ template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DI
 hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   constexpr int kBCw = NW * 16 * NJ;
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
-  const int total = n_col_tiles * p.B * p.Hkv;
+  // causal d = 64: column tiles paired per work-group (see the kernel)
+  const int n_units = p.causal && D < 128 ? (n_col_tiles + 1) / 2 : n_col_tiles;
+  const int total = n_units * p.B * p.Hkv;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
     hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, true>), dim3(total), dim3(NW * 64),
