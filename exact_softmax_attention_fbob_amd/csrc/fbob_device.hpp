@@ -30,11 +30,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Keeps the machine scheduler from hoisting loads across phases of a tile (it
 // otherwise front-loads every LDS fragment and runs out of registers).
-#ifndef FBOB_NO_SCHED_FENCE
 #define FBOB_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define FBOB_SCHED_FENCE() ((void)0)
-#endif
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Instruction groups for __builtin_amdgcn_sched_group_barrier: the scheduler
@@ -140,64 +136,30 @@ struct Tile {
   }
 };
 
-// Row-major operand fragment: 8 consecutive elements (row, col .. col+7),
-// col a multiple of 8.
+// fp32 operand fragments from an LDS tile (bf16 tiles are read through LdsLane
+// below, with precomputed offsets and the gfx950 transposing read).
+// Row-major: 8 consecutive elements (row, col .. col+7), col a multiple of 8.
 template <typename T, int D>
 __device__ __forceinline__ typename Elem<T>::frag lds_frag_row(const char* tile, int row, int col) {
-  using F = typename Elem<T>::frag;
-  if constexpr (sizeof(T) == 2) {
-    return *reinterpret_cast<const F*>(tile + Tile<T, D>::chunk_off(row, col >> 3));
-  } else {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::chunk_off(row, col >> 2));
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::chunk_off(row, (col >> 2) + 1));
-    return Elem<T>::from_f32(lo, hi);
-  }
+  static_assert(sizeof(T) == 4, "bf16 tiles are read through LdsLane");
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::chunk_off(row, col >> 2));
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::chunk_off(row, (col >> 2) + 1));
+  return Elem<T>::from_f32(lo, hi);
 }
 
-// Transposed operand fragment for a contraction over tile rows: lane (r, g)
-// gets X[row0 + k(g, e)][col0 + r], k(g, e) = 16 (e / 4) + 4 g + (e % 4).
-// bf16 uses the gfx950 transposing LDS read: in each 16-lane group, lane
-// (4 b + c) addresses 4 elements of row b at columns 4c..4c+3 and receives
-// column r of the 4 addressed rows.
+// Transposed, for a contraction over tile rows: lane (r, g) gets
+// X[row0 + k(g, e)][col0 + r], k(g, e) = 16 (e / 4) + 4 g + (e % 4).
 template <typename T, int D>
 __device__ __forceinline__ typename Elem<T>::frag lds_frag_tr(const char* tile, int row0, int col0,
                                                               int r, int g) {
-  using F = typename Elem<T>::frag;
-  if constexpr (sizeof(T) == 2) {
-#if FBOB_NO_TR_READ
-    F o;
+  static_assert(sizeof(T) == 4, "bf16 tiles are read through LdsLane");
+  typename Elem<T>::frag o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = row0 + 16 * (e >> 2) + 4 * g + (e & 3);
-      o[e] = *reinterpret_cast<const __bf16*>(tile + Tile<T, D>::elem_off(row, col0 + r));
-    }
-    return o;
-#else
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    const int b = r >> 2, c = r & 3;
-    const int off0 = Tile<T, D>::elem_off(row0 + 4 * g + b, col0 + 4 * c);
-    const int off1 = Tile<T, D>::elem_off(row0 + 16 + 4 * g + b, col0 + 4 * c);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)(reinterpret_cast<uintptr_t>(tile) + off0));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4*)(reinterpret_cast<uintptr_t>(tile) + off1));
-    F o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o[q] = lo[q];
-      o[4 + q] = hi[q];
-    }
-    return o;
-#endif
-  } else {
-    F o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = row0 + 16 * (e >> 2) + 4 * g + (e & 3);
-      o[e] = *reinterpret_cast<const float*>(tile + Tile<T, D>::elem_off(row, col0 + r));
-    }
-    return o;
+  for (int e = 0; e < 8; ++e) {
+    const int row = row0 + 16 * (e >> 2) + 4 * g + (e & 3);
+    o[e] = *reinterpret_cast<const float*>(tile + Tile<T, D>::elem_off(row, col0 + r));
   }
+  return o;
 }
 
 // Operand fragment straight from global memory: 8 consecutive elements of one
@@ -220,43 +182,6 @@ __device__ __forceinline__ typename Elem<T>::frag global_frag(const T* base, int
   }
   return o;
 }
-
-// ---------------------------------------------------------------------------
-// Tile staging: global (rows row0.., D columns, contiguous) -> registers -> LDS.
-// Rows at or past `nrows` are zero-filled.  kPer = 16-byte chunks per thread
-// (the last round may leave threads idle when the count does not divide).
-// ---------------------------------------------------------------------------
-template <typename T, int D, int ROWS, int NTHREADS>
-struct Stager {
-  static constexpr int kChunks = Tile<T, D>::kChunks;
-  static constexpr int kTotal = ROWS * kChunks;
-  static constexpr int kPer = (kTotal + NTHREADS - 1) / NTHREADS;
-  static constexpr bool kEven = kTotal % NTHREADS == 0;
-  u32x4 v[kPer];
-
-  __device__ __forceinline__ void load(const T* src, int row0, int nrows, int tid) {
-    const char* s = reinterpret_cast<const char*>(src);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int idx = tid + k * NTHREADS;
-      const int row = idx / kChunks, c = idx % kChunks;
-      if ((kEven || idx < kTotal) && row0 + row < nrows) {
-        v[k] = *reinterpret_cast<const u32x4*>(s + (int64_t)(row0 + row) * Tile<T, D>::kRowBytes + c * 16);
-      } else {
-        v[k] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* tile, int tid) const {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int idx = tid + k * NTHREADS;
-      const int row = idx / kChunks, c = idx % kChunks;
-      if (kEven || idx < kTotal)
-        *reinterpret_cast<u32x4*>(tile + Tile<T, D>::chunk_off(row, c)) = v[k];
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Staging of NT same-shaped tiles (ROWS rows each) in one pass: the NT * ROWS *
@@ -457,9 +382,9 @@ struct LdsLane {
   }
   __device__ __forceinline__ typename Elem<T>::frag tr(const char* tile, int db) const {
     if constexpr (sizeof(T) == 2) {
-#if FBOB_NO_TR_READ
-      return lds_frag_tr<T, D>(tile, 0, 16 * db, r, g);
-#else
+      // gfx950 transposing LDS read: in each 16-lane group, lane (4 b + c)
+      // addresses 4 elements of row b at columns 4 c .. 4 c + 3 and receives
+      // column r of the 4 addressed rows.
       typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
       const uintptr_t base = reinterpret_cast<uintptr_t>(tile) + tr_off(db);
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base));
@@ -471,7 +396,6 @@ struct LdsLane {
         o[4 + q] = hi[q];
       }
       return o;
-#endif
     } else {
       return lds_frag_tr<T, D>(tile, 0, 16 * db, r, g);
     }
