@@ -94,12 +94,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
         }
       }
     }
-    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mt = group_max(mt) * c1;
+    // This lane's maximum over its 8 keys of the block; m is shared by the four
+    // lanes of a row, so a lane above m + kSlack is enough to trigger the rescale,
+    // and the row maximum across lanes is only formed when it happens.
+    float ml = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * c1;
     // Raise the reference only when the new maximum would push a weight above
     // 2^kSlack (always on the first block, where m = -inf).
-    if (__any(mt > m + kSlack)) {
+    if (__any(ml > m + kSlack)) {
+      const float mt = group_max(ml);
       const float mn = fmaxf(m, mt);
       const float sc = fast_exp2(m - mn);
 #pragma unroll
