@@ -40,6 +40,11 @@ SMALL = [
     case("gqa_hq6_hkv2_n160_bf16_causal", 1, 6, 160, 64, "bf16", 20, causal=True, Hkv=2),
     case("mqa_hq3_hkv1_n96_d128_bf16", 1, 3, 96, 128, "bf16", 21, Hkv=1),
     case("n1000_u01_qk2_bf16", 1, 1, 1000, 64, "bf16", 22, scale_u=0.1, scale_qk=2.0),
+    # near one-hot rows: Q, K x 4 gives score std ~16 (most weights underflow to 0,
+    # the forward's reference maximum is raised many times along a row)
+    case("n500_h2_bf16_qk4_sharp", 1, 2, 500, 64, "bf16", 27, scale_qk=4.0),
+    case("n300_h2_bf16_qk4_sharp_causal", 1, 2, 300, 64, "bf16", 28, causal=True, scale_qk=4.0),
+    case("n260_d128_bf16_qk4_sharp", 1, 1, 260, 128, "bf16", 29, scale_qk=4.0),
     # a score scale that is not a power of two at d = 64 (tau applied on the VALU)
     case("n250_h2_bf16_tau0.1", 1, 2, 250, 64, "bf16", 23, tau=0.1),
     case("n190_h2_bf16_tau0.3_causal", 1, 2, 190, 64, "bf16", 24, causal=True, tau=0.3),
