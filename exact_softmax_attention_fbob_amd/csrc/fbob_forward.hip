@@ -5,8 +5,9 @@
 // FlashAttention blog ("FlashAttention 的反向传播设计"), sections 一 and 二: the
 // forward keeps only per-row statistics; FlashBoB notes, "关键设计" 1: D_i.
 //
-// Schedule: one work-group = NW waves, each wave owns 16 query rows (Q as MFMA
-// operand, O as fp32 accumulator in registers).  K and V tiles of BC keys are
+// Schedule: one work-group = NW waves, each wave owns 16 NI query rows (Q as MFMA
+// operand, O as fp32 accumulator in registers); every K and V fragment read from
+// LDS serves the NI row blocks of the wave.  K and V tiles of BC keys are
 // staged straight into LDS (double-buffered).  Scores are computed transposed
 // (S^T = K Q^T), so a lane owns one query row and 8 keys per 32-key block.
 // Online softmax in base 2 with a lazy running maximum: the weights are
@@ -27,12 +28,14 @@ namespace {
 constexpr float kSlack = 8.0f;  // log2 headroom before the reference max is raised
 
 // PRIO: raise the wave priority while the P V contraction MFMAs issue.
-template <typename T, int D, int NW, int BC, bool TP2, bool CAUSAL, bool PRIO = false>
+// NI: 16-row blocks per wave.
+template <typename T, int D, int NW, int BC, bool TP2, bool CAUSAL, bool PRIO = false, int NI = 1>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int group, int N,
                                                       float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int kBR = NW * 16;
+  constexpr int kRW = 16 * NI;                     // query rows per wave
+  constexpr int kBR = NW * kRW;
   constexpr int kTB = BC * Tile<T, D>::kRowBytes;  // bytes per staged tile
   constexpr int kDC = D / 32;
   constexpr int kDB = D / 16;
@@ -53,23 +56,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
   const T* const kv_bases[2] = {reinterpret_cast<const T*>(a.K) + kv_off,
                                 reinterpret_cast<const T*>(a.V) + kv_off};
 
-  const int iw0 = rt * kBR + w * 16;
-  const int i = iw0 + r;  // this lane's query row
+  const int iw0 = rt * kBR + w * kRW;
+  // this lane's query row in row block ib: iw0 + 16 ib + r
   // With TP2 (tau an exact power of two) the score operand is tau Q (exact).
-  F qf[kDC];
+  F qf[NI][kDC];
 #pragma unroll
-  for (int dc = 0; dc < kDC; ++dc) {
-    const F q0 = global_frag(Qh, i, N, D, 32 * dc + 8 * g);
-    qf[dc] = TP2 ? scale_frag<T>(q0, tau) : q0;
-  }
+  for (int ib = 0; ib < NI; ++ib)
+#pragma unroll
+    for (int dc = 0; dc < kDC; ++dc) {
+      const F q0 = global_frag(Qh, iw0 + 16 * ib + r, N, D, 32 * dc + 8 * g);
+      qf[ib][dc] = TP2 ? scale_frag<T>(q0, tau) : q0;
+    }
   const float c1 = TP2 ? kLog2e : tau * kLog2e;
   const F ones = ones_frag<T>();
 
-  f32x4 acc[kDB];
+  f32x4 acc[NI][kDB], accL[NI];  // accL: row sum of the weights (every q holds it)
+  float m[NI];                   // reference maximum of this lane's row (log2 units)
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) acc[db] = splat4(0.f);
-  f32x4 accL = splat4(0.f);  // row sum of the weights (every q holds it)
-  float m = -INFINITY;       // reference maximum of this lane's row (log2 units)
+  for (int ib = 0; ib < NI; ++ib) {
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) acc[ib][db] = splat4(0.f);
+    accL[ib] = splat4(0.f);
+    m[ib] = -INFINITY;
+  }
   const LdsLane<T, D> rd(r, g);
 
   int jend = N;
@@ -81,46 +90,72 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
     const bool edge = (j0 + 32 > N) || (CAUSAL && j0 + 31 > iw0);
     // Raw scores; the row maximum is taken before scaling (c1 > 0 commutes with
     // max), so each weight costs one FMA and one exp2.
-    f32x4 s[2];
+    f32x4 s[NI][2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
-      s[jb] = splat4(0.f);
 #pragma unroll
-      for (int dc = 0; dc < kDC; ++dc) s[jb] = E::mma(rd.row(Kt, jb, dc), qf[dc], s[jb]);
+      for (int ib = 0; ib < NI; ++ib) s[ib][jb] = splat4(0.f);
+#pragma unroll
+      for (int dc = 0; dc < kDC; ++dc) {
+        const F kf = rd.row(Kt, jb, dc);
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib) s[ib][jb] = E::mma(kf, qf[ib][dc], s[ib][jb]);
+      }
       if (edge) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + 16 * jb + 4 * g + q;
-          if (j >= N || (CAUSAL && j > i)) s[jb][q] = -INFINITY;
-        }
+        for (int ib = 0; ib < NI; ++ib)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = j0 + 16 * jb + 4 * g + q;
+            if (j >= N || (CAUSAL && j > iw0 + 16 * ib + r)) s[ib][jb][q] = -INFINITY;
+          }
       }
     }
     // This lane's maximum over its 8 keys of the block; m is shared by the four
     // lanes of a row, so a lane above m + kSlack is enough to trigger the rescale,
     // and the row maximum across lanes is only formed when it happens.
-    float ml = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * c1;
-    // Raise the reference only when the new maximum would push a weight above
-    // 2^kSlack (always on the first block, where m = -inf).
-    if (__any(ml > m + kSlack)) {
-      const float mt = group_max(ml);
-      const float mn = fmaxf(m, mt);
-      const float sc = fast_exp2(m - mn);
+    float ml[NI];
+    bool raise = false;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) acc[db] *= sc;
-      accL *= sc;
-      m = mn;
+    for (int ib = 0; ib < NI; ++ib) {
+      const f32x4* sb = s[ib];
+      ml[ib] = fmaxf(fmaxf(fmaxf(sb[0][0], sb[0][1]), fmaxf(sb[0][2], sb[0][3])),
+                     fmaxf(fmaxf(sb[1][0], sb[1][1]), fmaxf(sb[1][2], sb[1][3]))) * c1;
+      raise |= ml[ib] > m[ib] + kSlack;
     }
-    const float nm = -m;
-    F pB;
+    // Raise the reference only when the new maximum would push a weight above
+    // 2^kSlack (always on the first block, where m = -inf).  Every row block of the
+    // wave is brought up to its current maximum then (never lowered).
+    if (__any(raise)) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+      for (int ib = 0; ib < NI; ++ib) {
+        const float mn = fmaxf(m[ib], group_max(ml[ib]));
+        const float sc = fast_exp2(m[ib] - mn);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pB[4 * jb + q] = (T)fast_exp2(__builtin_fmaf(s[jb][q], c1, nm));
+        for (int db = 0; db < kDB; ++db) acc[ib][db] *= sc;
+        accL[ib] *= sc;
+        m[ib] = mn;
+      }
+    }
+    F pB[NI];
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib) {
+      const float nm = -m[ib];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pB[ib][4 * jb + q] = (T)fast_exp2(__builtin_fmaf(s[ib][jb][q], c1, nm));
+    }
     if constexpr (PRIO) FBOB_PRIO_HIGH();
-    accL = E::mma(ones, pB, accL);
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) acc[db] = E::mma(rd.tr(Vt, db), pB, acc[db]);
+    for (int ib = 0; ib < NI; ++ib) accL[ib] = E::mma(ones, pB[ib], accL[ib]);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const F vt = rd.tr(Vt, db);
+#pragma unroll
+      for (int ib = 0; ib < NI; ++ib) acc[ib][db] = E::mma(vt, pB[ib], acc[ib][db]);
+    }
     if constexpr (PRIO) FBOB_PRIO_LOW();
   };
 
@@ -137,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
 #pragma unroll
     for (int hs = 0; hs < BC / 32; ++hs) {
       const int js = j0 + 32 * hs;
-      if (!CAUSAL || js <= iw0 + 15)
+      if (!CAUSAL || js <= iw0 + kRW - 1)
         block32(cur + 32 * hs * Tile<T, D>::kRowBytes,
                 cur + kTB + 32 * hs * Tile<T, D>::kRowBytes, js);
     }
@@ -152,41 +187,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
 
   // Epilogue: O = acc / l, L = (m + log2 l) ln 2, and D = dO . O (fp32 O) when
   // dO is given (a uniform branch).
-  const float lsum = accL[0];
-  const float inv = 1.f / lsum;
   const bool with_d = a.dO != nullptr;
-  float dpart = 0.f;
-  if (i < N) {
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const int d0 = 16 * db + 4 * g;
-      const f32x4 o = acc[db] * inv;
-      *reinterpret_cast<f32x4*>(a.O + q_off + (int64_t)i * D + d0) = o;
-      if (with_d) {
-        const T* dOh = reinterpret_cast<const T*>(a.dO) + q_off;
+  for (int ib = 0; ib < NI; ++ib) {
+    const int i = iw0 + 16 * ib + r;
+    const float lsum = accL[ib][0];
+    const float inv = 1.f / lsum;
+    float dpart = 0.f;
+    if (i < N) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dpart += (float)dOh[(int64_t)i * D + d0 + q] * o[q];
+      for (int db = 0; db < kDB; ++db) {
+        const int d0 = 16 * db + 4 * g;
+        const f32x4 o = acc[ib][db] * inv;
+        *reinterpret_cast<f32x4*>(a.O + q_off + (int64_t)i * D + d0) = o;
+        if (with_d) {
+          const T* dOh = reinterpret_cast<const T*>(a.dO) + q_off;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dpart += (float)dOh[(int64_t)i * D + d0 + q] * o[q];
+        }
       }
     }
-  }
-  const float dsum = group_sum(dpart);
-  if (i < N && g == 0) {
-    a.L[(int64_t)bh * N + i] = (m + __log2f(lsum)) * kLn2;
-    if (with_d) a.D[(int64_t)bh * N + i] = dsum;
+    const float dsum = group_sum(dpart);
+    if (i < N && g == 0) {
+      a.L[(int64_t)bh * N + i] = (m[ib] + __log2f(lsum)) * kLn2;
+      if (with_d) a.D[(int64_t)bh * N + i] = dsum;
+    }
   }
 }
 
-template <typename T, int D, int NW, int BC, bool TP2, bool PRIO = false>
+template <typename T, int D, int NW, int BC, bool TP2, bool PRIO = false, int NI = 1>
 hipError_t launch_t(const Problem& p, const FwdArgs& a, hipStream_t s) {
-  constexpr int kBR = NW * 16;
+  constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
   const int total = n_row_tiles * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BC, TP2, true, PRIO>), dim3(total), dim3(NW * 64), 0, s, a,
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BC, TP2, true, PRIO, NI>), dim3(total), dim3(NW * 64), 0, s, a,
                        p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BC, TP2, false, PRIO>), dim3(total), dim3(NW * 64), 0, s, a,
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BC, TP2, false, PRIO, NI>), dim3(total), dim3(NW * 64), 0, s, a,
                        p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
 }
@@ -195,22 +234,33 @@ hipError_t launch_t(const Problem& p, const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
   if (p.bf16) {
+    // bf16 defaults: 32 query rows per wave (each K / V fragment read from LDS
+    // serves two row blocks), measured ~12 % faster than 16 at d = 64 and ~7 % at
+    // d = 128.
     if (p.d == 64) {
       if (tau_is_pow2(p.tau)) {
-        // raised wave priority over the P V MFMAs (~0.5 %); 1 selects the plain order
+        // 128-key stages and raised wave priority over the P V MFMAs; 1 selects 16
+        // rows per wave, 2 64-key stages, 3 the plain instruction order.
         const char* v = getenv("FBOB_TUNE_FWD");
-        if (v && atoi(v) == 1) return launch_t<__bf16, 64, 8, 64, true>(p, a, s);
-        return launch_t<__bf16, 64, 8, 64, true, true>(p, a, s);
+        const int cfg = v ? atoi(v) : 0;
+        if (cfg == 1) return launch_t<__bf16, 64, 8, 64, true, true, 1>(p, a, s);
+        if (cfg == 2) return launch_t<__bf16, 64, 8, 64, true, true, 2>(p, a, s);
+        if (cfg == 3) return launch_t<__bf16, 64, 8, 128, true, false, 2>(p, a, s);
+        return launch_t<__bf16, 64, 8, 128, true, true, 2>(p, a, s);
       }
-      return launch_t<__bf16, 64, 8, 64, false>(p, a, s);
+      return launch_t<__bf16, 64, 8, 128, false, false, 2>(p, a, s);
     }
+    // d = 128: 64-key stages; 1 and 2 select 16 rows per wave with 32-key stages
+    // and 8 or 4 waves per work-group, 3 16 rows per wave with 64-key stages, 4
+    // raised priority over the P V MFMAs, 5 128-key stages.
     const char* v = getenv("FBOB_TUNE_FWD_D128");
     const int cfg = v ? atoi(v) : 0;
-    // d = 128: 64-key stages (measured ~2 % faster than 32); 1 and 2 select 32-key
-    // stages with 8 or 4 waves per work-group.
     if (cfg == 1) return launch_t<__bf16, 128, 8, 32, false>(p, a, s);
     if (cfg == 2) return launch_t<__bf16, 128, 4, 32, false>(p, a, s);
-    return launch_t<__bf16, 128, 8, 64, false>(p, a, s);
+    if (cfg == 3) return launch_t<__bf16, 128, 8, 64, false>(p, a, s);
+    if (cfg == 4) return launch_t<__bf16, 128, 8, 64, false, true, 2>(p, a, s);
+    if (cfg == 5) return launch_t<__bf16, 128, 8, 128, false, false, 2>(p, a, s);
+    return launch_t<__bf16, 128, 8, 64, false, false, 2>(p, a, s);
   }
   if (p.d == 64) return launch_t<float, 64, 4, 32, false>(p, a, s);
   return launch_t<float, 128, 4, 32, false>(p, a, s);

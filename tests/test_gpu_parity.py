@@ -193,7 +193,7 @@ TUNE_VARIANTS = [("FBOB_TUNE_P1", v) for v in (1, 2, 3, 4, 5, 6)] + \
     [("FBOB_TUNE_P2", v) for v in (1, 2, 3, 4, 5)] + \
     [("FBOB_TUNE_P1_D128", v) for v in (1, 2)] + \
     [("FBOB_TUNE_P2_D128", v) for v in (1, 2, 3)] + \
-    [("FBOB_TUNE_FWD_D128", v) for v in (1, 2)] + [("FBOB_TUNE_FWD", 1)]
+    [("FBOB_TUNE_FWD_D128", v) for v in (1, 2, 3, 4, 5)] + [("FBOB_TUNE_FWD", v) for v in (1, 2, 3)]
 
 
 @pytest.mark.parametrize("var,val", TUNE_VARIANTS, ids=[f"{a}={b}" for a, b in TUNE_VARIANTS])
