@@ -460,6 +460,17 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of the eight values of two score fragments.  The IEEE-2019 maximum
+// (NaN-propagating) maps to gfx950's three-input v_maximum3_f32, four
+// instructions for eight values; fmaxf would first canonicalize every MFMA result
+// with a move of its own.
+__device__ __forceinline__ float max8(const f32x4& a, const f32x4& b) {
+  const float m0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[0], a[1]), a[2]);
+  const float m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a[3], b[0]), b[1]);
+  const float m2 = __builtin_elementwise_maximum(b[2], b[3]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2);
+}
+
 // Work-group index remapped so that consecutive logical blocks run on the same
 // XCD (the dispatcher hands block b to XCD b % 8): blocks of one head then share
 // that XCD's L2 for the streamed operand tiles.  Bijective for any `total`.

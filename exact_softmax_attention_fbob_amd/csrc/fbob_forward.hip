@@ -72,12 +72,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
 
   f32x4 acc[NI][kDB], accL[NI];  // accL: row sum of the weights (every q holds it)
   float m[NI];                   // reference maximum of this lane's row (log2 units)
+  float thr[NI];                 // (m + kSlack) / c1: the raw score that forces a rescale
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
 #pragma unroll
     for (int db = 0; db < kDB; ++db) acc[ib][db] = splat4(0.f);
     accL[ib] = splat4(0.f);
     m[ib] = -INFINITY;
+    thr[ib] = -INFINITY;
   }
   const LdsLane<T, D> rd(r, g);
 
@@ -114,14 +116,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
     // This lane's maximum over its 8 keys of the block; m is shared by the four
     // lanes of a row, so a lane above m + kSlack is enough to trigger the rescale,
     // and the row maximum across lanes is only formed when it happens.
+    // (raw scores: c1 > 0, so the test against thr = (m + kSlack) / c1 needs no
+    // scaling; every row's first block holds a valid key, so m is finite after it)
     float ml[NI];
     bool raise = false;
 #pragma unroll
     for (int ib = 0; ib < NI; ++ib) {
-      const f32x4* sb = s[ib];
-      ml[ib] = fmaxf(fmaxf(fmaxf(sb[0][0], sb[0][1]), fmaxf(sb[0][2], sb[0][3])),
-                     fmaxf(fmaxf(sb[1][0], sb[1][1]), fmaxf(sb[1][2], sb[1][3]))) * c1;
-      raise |= ml[ib] > m[ib] + kSlack;
+      ml[ib] = max8(s[ib][0], s[ib][1]);
+      raise |= ml[ib] > thr[ib];
     }
     // Raise the reference only when the new maximum would push a weight above
     // 2^kSlack (always on the first block, where m = -inf).  Every row block of the
@@ -129,12 +131,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
     if (__any(raise)) {
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) {
-        const float mn = fmaxf(m[ib], group_max(ml[ib]));
+        const float mn = fmaxf(m[ib], group_max(ml[ib]) * c1);
         const float sc = fast_exp2(m[ib] - mn);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) acc[ib][db] *= sc;
         accL[ib] *= sc;
         m[ib] = mn;
+        thr[ib] = (mn + kSlack) / c1;
       }
     }
     F pB[NI];
