@@ -1,5 +1,6 @@
 """Small drivers for hardware-counter runs (run under rocprofv3 on one MI355X).
 
+    python -m exact_softmax_attention_fbob_amd.profiling forward [--workload W] [--launches K]
     python -m exact_softmax_attention_fbob_amd.profiling pass1 [--workload W] [--launches K]
     python -m exact_softmax_attention_fbob_amd.profiling pass2 [--workload W] [--launches K]
     python -m exact_softmax_attention_fbob_amd.profiling copy [--mib M] [--launches K]
@@ -7,8 +8,8 @@
         --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv --copy-mib M \
         [--workload W] [--out profiles/pass1_hbm_traffic.json]
 
-`pass1`/`pass2` run the forward once and then the chosen BoB pass K times on the
-seeded inputs of a workload; `copy` runs a plain device-to-device copy of M MiB
+`forward`/`pass1`/`pass2` run the forward once and then the chosen kernel K times
+on the seeded inputs of a workload (Pass 1 runs once in every case); `copy` runs a plain device-to-device copy of M MiB
 (read M MiB, write M MiB) as the calibration kernel for the byte counters;
 `record` turns rocprofv3 counter_collection CSVs (FETCH_SIZE / WRITE_SIZE, KiB
 per dispatch) into bytes per launch of the chosen kernel, scaled by what the
@@ -56,6 +57,8 @@ def _setup(workload):
 def run_pass(which, workload, launches):
     import torch
     w, fb, args, O, L, D = _setup(workload)
+    for _ in range(launches if which == "forward" else 0):
+        fb.forward(*args[:4], w.tau, w.causal)
     p1 = fb.bob_pass1(*args, O, L, D, w.tau, w.causal)
     for _ in range(launches if which == "pass1" else 0):
         fb.bob_pass1(*args, O, L, D, w.tau, w.causal)
@@ -122,7 +125,7 @@ def record(a):
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
-    for name in ("pass1", "pass2"):
+    for name in ("forward", "pass1", "pass2"):
         p = sub.add_parser(name)
         p.add_argument("--workload", default="h12_n16384_d64_bf16_u01")
         p.add_argument("--launches", type=int, default=3)
@@ -140,7 +143,7 @@ def main():
     p.add_argument("--workload", default="h12_n16384_d64_bf16_u01")
     p.add_argument("--out", default=os.path.join(ROOT, "profiles", "pass1_hbm_traffic.json"))
     a = ap.parse_args()
-    if a.cmd in ("pass1", "pass2"):
+    if a.cmd in ("forward", "pass1", "pass2"):
         run_pass(a.cmd, a.workload, a.launches)
     elif a.cmd == "copy":
         run_copy(a.mib, a.launches)
