@@ -98,6 +98,26 @@ def test_backward_small_cases_full_oracle(w):
     assert all(v <= tol for v in errs.values()), errs
 
 
+DQ_VARIANTS = [("FBOB_TUNE_DQ", v) for v in (1, 2)] + [("FBOB_TUNE_DQ_D128", v) for v in (1, 2)]
+
+
+@pytest.mark.parametrize("var,val", DQ_VARIANTS, ids=[f"{a}={b}" for a, b in DQ_VARIANTS])
+def test_backward_row_pass_variants(var, val, monkeypatch):
+    """Every compiled layout of the row pass (rows per wave, stage size) against the
+    oracle, on a ragged tail and on a causal grouped-query case."""
+    d = 128 if var.endswith("D128") else 64
+    monkeypatch.setenv(var, str(val))
+    for w in (case(f"dqv_n300_b2_h2_d{d}", 2, 2, 300, d, "bf16", 81),
+              case(f"dqv_gqa_hq4_hkv2_n200_d{d}_causal", 1, 4, 200, d, "bf16", 82, causal=True,
+                   Hkv=2)):
+        U.say(f"[grad] {var}={val} {w.name}")
+        inp = U.make_inputs(w)
+        gpu = run_grad(U.to_device(inp, w.dtype), w.tau, w.causal)
+        errs = compare(gpu, oracle_grad(inp, w), w)
+        U.say(f"[grad] {var}={val} {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+
+
 def _check_column_sums(w, inp, gpu):
     """sum_j dK_j = 0 and sum_j dV_j = sum over the group's rows of dO (exact)."""
     hkv = w.extra.get("Hkv", w.H)
