@@ -132,6 +132,25 @@ def test_large_sampled_rows_and_invariants(name):
     _check_invariants(gpu)
 
 
+@pytest.mark.parametrize("name", ["pages_causal_b4_h12_n16384_d64_bf16",
+                                  "pages_causal_b4_h12_n16384_d128_bf16"])
+def test_pages_causal_shape_full_two_heads(name):
+    """The pages' causal benchmark shape (B=4, H=12, N=16384): full oracle on the first
+    head of the first batch and the last head of the last batch (blocked rows, all six
+    outputs), sampled rows on every head, and the column-sum invariants."""
+    w = W[name]
+    U.say(f"[parity] {w.name}")
+    inp = U.make_inputs(w)
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    ref = U.oracle_full(inp, w, heads=[(0, 0), (w.B - 1, w.H - 1)], blocked=True)
+    errs = U.compare_full(gpu, ref, w, keys=U.ALL_KEYS)
+    U.say(f"[parity] {w.name} heads (0,0), ({w.B - 1},{w.H - 1}): "
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+    _check_sampled_rows(w, inp, gpu, n_rows=4)
+    _check_invariants(gpu)
+
+
 def test_bitwise_deterministic():
     import torch
     import exact_softmax_attention_fbob_amd as fb
