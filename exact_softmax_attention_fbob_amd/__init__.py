@@ -59,6 +59,8 @@ def _check_inputs(Q, K, V, dO, UQ=None, UK=None, UV=None):
     for x in ins:
         if not x.is_cuda:
             raise ValueError("all tensors must be on the GPU")
+        if x.device != Q.device:
+            raise ValueError("all tensors must be on the same GPU")
         if not x.is_contiguous():
             raise ValueError("all tensors must be contiguous ([B, H, N, d], d fastest)")
         if x.dtype != Q.dtype:
@@ -76,10 +78,12 @@ def _check_inputs(Q, K, V, dO, UQ=None, UK=None, UV=None):
     return B, Hq, Hkv, N, d
 
 
-def _check_f32(x, shape, name):
+def _check_f32(x, shape, name, dev):
     torch = _torch()
     if x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda:
         raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if x.device != dev:
+        raise ValueError(f"{name} must be on the inputs' GPU ({dev})")
     if tuple(x.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
 
@@ -88,12 +92,16 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream():
-    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+def _stream(dev):
+    """torch's current stream on the inputs' device."""
+    return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
 
 
-def _call(fn, *args):
-    st = fn(*args)
+def _call(dev, fn, *args):
+    """Call a library entry point with the inputs' device current (the kernels launch
+    on the current device, into the given stream of that device)."""
+    with _torch().cuda.device(dev):
+        st = fn(*args)
     if st != 0:
         raise FbobError(st)
 
@@ -113,9 +121,9 @@ def forward(Q, K, V, dO=None, tau=None, causal=False):
     O = torch.empty((B, Hq, N, d), dtype=torch.float32, device=Q.device)
     L = torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
     D = None if dO is None else torch.empty((B, Hq, N), dtype=torch.float32, device=Q.device)
-    _call(lib.fbob_forward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
-          _p(Q), _p(K), _p(V), None if dO is None else _p(dO), _p(O), _p(L),
-          None if D is None else _p(D), _stream())
+    _call(Q.device, lib.fbob_forward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), None if dO is None else _p(dO), _p(O), _p(L),
+          None if D is None else _p(D), _stream(Q.device))
     return O, L, D
 
 
@@ -129,23 +137,23 @@ def backward(Q, K, V, dO, O, L, tau=None, causal=False):
     torch = _torch()
     lib = load_library()
     B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO)
-    _check_f32(O, (B, Hq, N, d), "O")
-    _check_f32(L, (B, Hq, N), "L")
     dev = Q.device
+    _check_f32(O, (B, Hq, N, d), "O", dev)
+    _check_f32(L, (B, Hq, N), "L", dev)
     out = dict(dQ=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
                dK=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
                dV=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
                D=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
-    _call(lib.fbob_backward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
-          _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L),
-          _p(out["dQ"]), _p(out["dK"]), _p(out["dV"]), _p(out["D"]), _stream())
+    _call(dev, lib.fbob_backward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L),
+          _p(out["dQ"]), _p(out["dK"]), _p(out["dV"]), _p(out["D"]), _stream(dev))
     return out
 
 
-def _row_state(O, L, D, B, Hq, N, d):
-    _check_f32(O, (B, Hq, N, d), "O")
-    _check_f32(L, (B, Hq, N), "L")
-    _check_f32(D, (B, Hq, N), "D")
+def _row_state(O, L, D, B, Hq, N, d, dev):
+    _check_f32(O, (B, Hq, N, d), "O", dev)
+    _check_f32(L, (B, Hq, N), "L", dev)
+    _check_f32(D, (B, Hq, N), "D", dev)
 
 
 def bob(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, out=None):
@@ -156,9 +164,9 @@ def bob(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, out=None):
     torch = _torch()
     lib = load_library()
     B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
-    _row_state(O, L, D, B, Hq, N, d)
+    dev = Q.device
+    _row_state(O, L, D, B, Hq, N, d, dev)
     if out is None:
-        dev = Q.device
         out = dict(dQt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
                    dKt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
                    dVt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
@@ -168,11 +176,11 @@ def bob(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, out=None):
     else:
         for k, shp in (("dQt", (B, Hq, N, d)), ("dKt", (B, Hkv, N, d)), ("dVt", (B, Hkv, N, d)),
                        ("ddOt", (B, Hq, N, d)), ("alpha", (B, Hq, N)), ("E", (B, Hq, N))):
-            _check_f32(out[k], shp, k)
-    _call(lib.fbob_bob, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+            _check_f32(out[k], shp, k, dev)
+    _call(dev, lib.fbob_bob, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
           _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
           _p(out["dQt"]), _p(out["dKt"]), _p(out["dVt"]), _p(out["ddOt"]),
-          _p(out["alpha"]), _p(out["E"]), _stream())
+          _p(out["alpha"]), _p(out["E"]), _stream(dev))
     return out
 
 
@@ -181,15 +189,15 @@ def bob_pass1(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False):
     torch = _torch()
     lib = load_library()
     B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
-    _row_state(O, L, D, B, Hq, N, d)
     dev = Q.device
+    _row_state(O, L, D, B, Hq, N, d, dev)
     out = dict(dQt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
                ddOt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
                alpha=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
                E=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
-    _call(lib.fbob_bob_pass1, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
-          _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
-          _p(out["dQt"]), _p(out["ddOt"]), _p(out["alpha"]), _p(out["E"]), _stream())
+    _call(dev, lib.fbob_bob_pass1, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L),
+          _p(D), _p(out["dQt"]), _p(out["ddOt"]), _p(out["alpha"]), _p(out["E"]), _stream(dev))
     return out
 
 
@@ -198,12 +206,12 @@ def bob_pass2(Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, tau=None, causal=False):
     torch = _torch()
     lib = load_library()
     B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
-    for x, name in ((L, "L"), (D, "D"), (alpha, "alpha"), (E, "E")):
-        _check_f32(x, (B, Hq, N), name)
     dev = Q.device
+    for x, name in ((L, "L"), (D, "D"), (alpha, "alpha"), (E, "E")):
+        _check_f32(x, (B, Hq, N), name, dev)
     out = dict(dKt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
                dVt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev))
-    _call(lib.fbob_bob_pass2, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
-          _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(L), _p(D), _p(alpha), _p(E),
-          _p(out["dKt"]), _p(out["dVt"]), _stream())
+    _call(dev, lib.fbob_bob_pass2, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(L), _p(D),
+          _p(alpha), _p(E), _p(out["dKt"]), _p(out["dVt"]), _stream(dev))
     return out
