@@ -195,6 +195,38 @@ def test_empty_problem_writes_nothing():
     assert all(v.numel() == 0 for v in out.values())
 
 
+ZERO_CASES = [case("zero_n300_h2_bf16", 1, 2, 300, 64, "bf16", 41),
+              case("zero_n200_h2_bf16_causal", 1, 2, 200, 64, "bf16", 42, causal=True),
+              case("zero_n150_d128_bf16", 1, 1, 150, 128, "bf16", 43),
+              case("zero_gqa_hq4_hkv2_n130_f32_causal", 1, 4, 130, 64, "f32", 44, causal=True,
+                   Hkv=2)]
+
+
+@pytest.mark.parametrize("w", ZERO_CASES, ids=[w.name for w in ZERO_CASES])
+def test_zero_directions_give_exact_zeros(w):
+    """Degenerate directions: with U_Q = U_K = U_V = 0, Phi vanishes identically and every
+    BoB output (dQ~, dK~, dV~, ddO~, alpha, E) is exactly zero; with dO = 0 every
+    first-order gradient and D are exactly zero.  No rounding enters either (every
+    product involves an exact zero), so the check is bitwise."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    U.say(f"[parity] {w.name}")
+    dev = U.to_device(U.make_inputs(w), w.dtype)
+    Q, K, V, dO = dev["Q"], dev["K"], dev["V"], dev["dO"]
+    zq, zk = torch.zeros_like(dev["UQ"]), torch.zeros_like(dev["UK"])
+    O, L, D = fb.forward(Q, K, V, dO, w.tau, w.causal)
+    out = fb.bob(Q, K, V, dO, zq, zk, zk, O, L, D, w.tau, w.causal)
+    g = fb.backward(Q, K, V, torch.zeros_like(dO), O, L, w.tau, w.causal)
+    torch.cuda.synchronize()
+    for name, t in list(out.items()) + list(g.items()):
+        nz = int((t != 0).sum())
+        assert nz == 0, f"{name}: {nz} nonzero elements"
+    # and the row state is not degenerate: the same call with the drawn U is not zero
+    full = fb.bob(Q, K, V, dO, dev["UQ"], dev["UK"], dev["UV"], O, L, D, w.tau, w.causal)
+    torch.cuda.synchronize()
+    assert all(bool((t != 0).any()) for t in full.values())
+
+
 def test_n1m_single_head_sampled_rows_and_invariants():
     """N = 2^20 (four times the long-context workload), B=1 H=1 d=64 bf16."""
     w = case("h1_n1048576_d64_bf16", 1, 1, 1 << 20, 64, "bf16", 1006)
