@@ -45,6 +45,9 @@ SMALL = [
     case("n500_h2_bf16_qk4_sharp", 1, 2, 500, 64, "bf16", 27, scale_qk=4.0),
     case("n300_h2_bf16_qk4_sharp_causal", 1, 2, 300, 64, "bf16", 28, causal=True, scale_qk=4.0),
     case("n260_d128_bf16_qk4_sharp", 1, 1, 260, 128, "bf16", 29, scale_qk=4.0),
+    # Q, K x 8: score std ~64, rows effectively one-hot, large jumps of the row maximum
+    case("n200_h2_bf16_qk8_extreme", 1, 2, 200, 64, "bf16", 30, scale_qk=8.0),
+    case("n180_h2_bf16_qk8_extreme_causal", 1, 2, 180, 64, "bf16", 31, causal=True, scale_qk=8.0),
     # a score scale that is not a power of two at d = 64 (tau applied on the VALU)
     case("n250_h2_bf16_tau0.1", 1, 2, 250, 64, "bf16", 23, tau=0.1),
     case("n190_h2_bf16_tau0.3_causal", 1, 2, 190, 64, "bf16", 24, causal=True, tau=0.3),
