@@ -65,10 +65,10 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """Time the fp64 oracle on a bounded sample: blocks of 256 full-width rows of
-    head 0 (forward row state + all BoB row outputs + the block's share of
-    dK~/dV~), until ``budget_s`` seconds have passed."""
+def cpu_baseline(w, budget_s: float = 15.0, max_heads: int = 4):
+    """Time the fp64 oracle on a bounded sample: blocks of 256 full-width rows
+    (forward row state + all BoB row outputs + the block's share of dK~/dV~), head
+    after head (at most ``max_heads``), until ``budget_s`` seconds have passed."""
     import numpy as np
     import oracle
     import workloads
@@ -78,25 +78,42 @@ def cpu_baseline(w, budget_s: float = 12.0):
                        if i.get("user_api") == "blas"), default=1)
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    inp = workloads.make_inputs(w, heads=[0])
-    h = {k: v[0].astype(np.float64) for k, v in inp.items()}
+    H = w.H
+    group = H // w.extra.get("Hkv", H)
+    qs = list(range(min(max_heads, w.B * H)))          # flat query heads b * H + h
+    kv = {f: (f // H) * H + (f % H) // group for f in qs}  # their key/value heads in the draw
+    need = sorted(set(qs) | set(kv.values()))
+    pos = {f: k for k, f in enumerate(need)}
+    inp = {k: v.astype(np.float64) for k, v in workloads.make_inputs(w, heads=need).items()}
+
+    def pairs(r0, r1):  # (i, j) pairs of rows r0 .. r1 - 1
+        return (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2.0 if w.causal else float(r1 - r0) * w.N
+
     block = 256
-    rows_done = 0
+    rows_done, heads_touched, pair_count = 0, 0, 0.0
     t0 = time.perf_counter()
-    while rows_done < w.N and time.perf_counter() - t0 < budget_s:
-        rows = np.arange(rows_done, min(w.N, rows_done + block))
-        oracle.bob_row_block(h["Q"], h["K"], h["V"], h["dO"], h["UQ"], h["UK"], h["UV"],
-                             w.tau, rows, w.causal)
-        rows_done += len(rows)
+    for f in qs:
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        heads_touched += 1
+        qh = {k: inp[k][pos[f]] for k in ("Q", "dO", "UQ")}
+        kh = {k: inp[k][pos[kv[f]]] for k in ("K", "V", "UK", "UV")}
+        r0 = 0
+        while r0 < w.N and time.perf_counter() - t0 < budget_s:
+            r1 = min(w.N, r0 + block)
+            oracle.bob_row_block(qh["Q"], kh["K"], kh["V"], qh["dO"], qh["UQ"], kh["UK"],
+                                 kh["UV"], w.tau, np.arange(r0, r1), w.causal)
+            pair_count += pairs(r0, r1)
+            rows_done += r1 - r0
+            r0 = r1
     dt = time.perf_counter() - t0
-    # same FLOP formula, for the (i, j) pairs of the sampled rows
-    pairs = rows_done * (rows_done + 1) / 2.0 if w.causal else float(rows_done) * w.N
-    flops = 42.0 * pairs * w.d
+    flops = 42.0 * pair_count * w.d  # the bench step's FLOP formula over the sampled pairs
+    full = 42.0 * pairs(0, w.N) * w.d * w.B * w.H
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows_done} of {w.N} rows of head 0 of {w.B * w.H} heads "
-                      f"({flops:.3e} FLOP, {dt:.1f} s, fp64 numpy)",
-            "extrapolated_full_step_s": dt * (w.N / rows_done) * w.B * w.H}
+            "sample": f"{rows_done} rows in {heads_touched} of {w.B * w.H} heads, "
+                      f"{w.N} rows per head ({flops:.3e} FLOP, {dt:.1f} s, fp64 numpy)",
+            "extrapolated_full_step_s": dt * full / flops}
 
 
 def time_extras(fb, lib, T, O, L, w, Hkv, n2d, bob_ms, fwd_ms, stream, steps):

@@ -80,4 +80,11 @@ def test_cpu_baseline_on_a_tiny_workload():
     r = bench.cpu_baseline(w, budget_s=0.5)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
-    assert "of 96 rows of head 0" in r["sample"]
+    assert r["sample"].startswith("192 rows in 2 of 2 heads"), r["sample"]
+    # a GQA workload maps query heads to their key/value heads and a causal one counts
+    # only the unmasked pairs
+    g = workloads.small("tiny_gqa", B=1, H=4, N=64, d=64, dtype="bf16", seed=6, causal=True,
+                        extra={"Hkv": 2})
+    r = bench.cpu_baseline(g, budget_s=30.0, max_heads=3)
+    assert r["sample"].startswith("192 rows in 3 of 4 heads"), r["sample"]
+    assert r["extrapolated_full_step_s"] > 0
