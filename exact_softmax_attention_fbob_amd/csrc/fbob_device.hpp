@@ -263,7 +263,7 @@ struct MultiStager {
 // is addressed as uniform base + lane offset; only a stage that crosses the end
 // takes the per-lane clamp.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int ROWS, int NT, int NW>
+template <typename T, int D, int ROWS, int NT, int NW, bool ASM_DMA = false>
 struct DirectStager {
   static constexpr int kRB = Tile<T, D>::kRowBytes;
   static constexpr int kChunks = Tile<T, D>::kChunks;
@@ -298,14 +298,33 @@ struct DirectStager {
       lds_off[k] = tensor * kTileBytes + rg * 1024;
     }
   }
-  __device__ __forceinline__ void load(char* tiles, int row0, int nrows, int64_t byte_off = 0) const {
+  // One 16-byte-per-lane global -> LDS transfer into the 1 KiB block at `lds`.
+  __device__ __forceinline__ static void dma(const char* gp, char* lds) {
     typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(1))) void glb_void;
+    if constexpr (ASM_DMA) {
+      // The same instruction written out.  The compiler does not track it, so it
+      // neither holds each transposing LDS read (which it cannot prove disjoint from
+      // the transfer) until the transfer lands, nor orders other memory accesses
+      // around it (no memory clobber).  That is sound under the staging discipline
+      // every caller follows: the transfer targets the buffer that no wave reads
+      // before the next barrier, the caller's s_waitcnt(0) precedes that barrier,
+      // and the barrier (a fence) keeps later reads of the buffer after it; volatile
+      // asm is never moved across the waitcnt or the barrier.  The instruction
+      // writes no VGPR and reads its address at issue.  M0 (the LDS address) is set
+      // by the compiler for the operand, one wait state before the load.
+      const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds;
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gp), "{m0}"(m0));
+    } else {
+      __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)lds, 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void load(char* tiles, int row0, int nrows, int64_t byte_off = 0) const {
     if (row0 + ROWS <= nrows) {  // wave-uniform: the whole stage lies inside the tensor
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const char* gp = base[k] + byte_off + (int64_t)(row0 + row_blk[k]) * kRB + voff[k];
-        __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)(tiles + lds_off[k]), 16, 0, 0);
+        dma(gp, tiles + lds_off[k]);
       }
     } else {
 #pragma unroll
@@ -314,7 +333,7 @@ struct DirectStager {
         const int rb = row0 + row_blk[k];
         const int shift = max(rb + lrow - (nrows - 1), 0);
         const char* gp = base[k] + byte_off + ((int64_t)rb - shift) * kRB + voff[k];
-        __builtin_amdgcn_global_load_lds((glb_void*)gp, (lds_void*)(tiles + lds_off[k]), 16, 0, 0);
+        dma(gp, tiles + lds_off[k]);
       }
     }
   }

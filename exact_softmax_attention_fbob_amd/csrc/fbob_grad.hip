@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
   };
 
   using RegStager = MultiStager<T, D, BC, 2, kThreads>;
-  using DirStager = DirectStager<T, D, BC, 2, NW>;
+  using DirStager = DirectStager<T, D, BC, 2, NW, true>;
   typename std::conditional<DIRECT, DirStager, RegStager>::type st;
   if constexpr (DIRECT) st.init(kv_bases, w, lane);
   else st.init(kv_bases, tid);
@@ -253,12 +253,15 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
   const T* const q_bases[2] = {reinterpret_cast<const T*>(a.Q) + q0,
                                reinterpret_cast<const T*>(a.dO) + q0};
   using RegStager = MultiStager<T, D, BRS, 2, kThreads>;
-  using DirStager = DirectStager<T, D, BRS, 2, NW>;
+  using DirStager = DirectStager<T, D, BRS, 2, NW, true>;
   typename std::conditional<DIRECT, DirStager, RegStager>::type st;
   if constexpr (DIRECT) st.init(q_bases, w, lane);
   else st.init(q_bases, tid);
   const int64_t s0 = ((int64_t)b * Hq + (int64_t)hk * group) * N;
   float sl = 0.f, sd = 0.f;
+  // The raw L and D stay in registers until store_step: deriving the seeds here
+  // would make this wave wait for every load it has in flight (the tiles'
+  // included) before it computes the current stage.
   auto load_step = [&](int step, char* buf) {
     const int hq = step / nrc;
     const int i0 = i_begin + (step % nrc) * BRS;
@@ -266,17 +269,17 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
     else st.load(i0, N, hq * q_head);
     if (tid < BRS) {
       const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
-      sl = -a.L[ri] * kLog2e;
-      sd = -a.D[ri];
+      sl = a.L[ri];
+      sd = a.D[ri];
     }
   };
+  // (DIRECT: the caller has waited for every load of the step.)
   auto store_step = [&](char* buf) {
-    if constexpr (DIRECT) wait_all_memory();
-    else st.store(buf);
+    if constexpr (!DIRECT) st.store(buf);
     if (tid < BRS) {
       float* sp = reinterpret_cast<float*>(buf + 2 * kTB);
-      sp[tid] = sl;
-      sp[BRS + tid] = sd;
+      sp[tid] = -sl * kLog2e;
+      sp[BRS + tid] = -sd;
     }
   };
 
@@ -344,6 +347,7 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
   };
 
   load_step(0, lds[0]);
+  if constexpr (DIRECT) wait_all_memory();
   store_step(lds[0]);
   __syncthreads();
   auto step = [&](int t, char* cur, char* nxt) {
@@ -355,6 +359,9 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
       const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
       if (active) chunk(cur, i0, sc);
     }
+    // Unconditional, so that the compiler sees every load of the step complete
+    // at the barrier (on the last step nothing is outstanding).
+    if constexpr (DIRECT) wait_all_memory();
     if (more) store_step(nxt);
     __syncthreads();
   };

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
                                  reinterpret_cast<const T*>(a.UQ) + q0};
     // Q, dO, U_Q tiles: registers + ds_write (MultiStager) or direct global -> LDS.
     using RegStager = MultiStager<T, D, BRS, 3, kThreads>;
-    using DirStager = DirectStager<T, D, BRS, 3, NW>;
+    using DirStager = DirectStager<T, D, BRS, 3, NW, !CAUSAL>;
     typename std::conditional<DIRECT, DirStager, RegStager>::type st;
     if constexpr (DIRECT) st.init(q_bases, w, lane);
     else st.init(q_bases, tid);
@@ -140,19 +140,23 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       const int i0 = i_begin + (step % nrc) * BRS;
       if constexpr (DIRECT) st.load(buf, i0, N, hq * q_head);
       else st.load(i0, N, hq * q_head);
+      // The raw values stay in registers until store_step: deriving the seeds here
+      // would make this wave wait for every load it has in flight (the tiles'
+      // included) before it computes the current stage.
       if (tid < BRS) {
         const int64_t ri = s0 + (int64_t)hq * N + min(i0 + tid, N - 1);
-        const float L = a.L[ri], Dv = a.D[ri], al = a.alpha[ri], Ev = a.E[ri];
-        scal = f32x4{-L * kLog2e, -Dv, -al * inv_tau, -(Ev + al * Dv)};
+        scal = f32x4{a.L[ri], a.D[ri], a.alpha[ri], a.E[ri]};
       }
     };
+    // (DIRECT: the caller has waited for every load of the step.)
     auto store_step = [&](char* buf) {
-      if constexpr (DIRECT) wait_all_memory();
-      else st.store(buf);
+      if constexpr (!DIRECT) st.store(buf);
       if (tid < BRS) {
+        const float L = scal[0], Dv = scal[1], al = scal[2], Ev = scal[3];
+        const f32x4 seed = {-L * kLog2e, -Dv, -al * inv_tau, -(Ev + al * Dv)};
         float* sp = reinterpret_cast<float*>(buf + 3 * kTB);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) sp[m * BRS + tid] = scal[m];
+        for (int m = 0; m < 4; ++m) sp[m * BRS + tid] = seed[m];
       }
     };
 
@@ -240,6 +244,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
     };
 
     load_step(0, lds[0]);
+    if constexpr (DIRECT) wait_all_memory();
     store_step(lds[0]);
     __syncthreads();
 
@@ -252,6 +257,9 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
         const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
         if (active) chunk(cur, i0, sc);
       }
+      // Unconditional, so that the compiler sees every load of the step complete
+      // at the barrier (on the last step nothing is outstanding).
+      if constexpr (DIRECT) wait_all_memory();
       if (more) store_step(nxt);
       __syncthreads();
     };
