@@ -38,8 +38,9 @@ Readings where the pages leave a step open (each is listed again in the design doc):
 
 Parity pins (tests/test_oracle_pins.py): central finite differences of Phi and of
 <O, dO>, a symbolic (sympy) derivation on a 2x2 case, torch autograd double
-backward in float64, linearity in U, the affine identities, exact invariants and
-the U_Q = U_K = 0 and N = 1 special cases.  No function here is "parity unpinned".
+backward in float64, linearity in U, the affine identities, exact invariants (among
+them E_i = dO_i . ddO~_i - alpha_i D_i, which ties E to ddO~) and the U_Q = U_K = 0
+and N = 1 special cases.  No function here is "parity unpinned".
 """
 
 from __future__ import annotations

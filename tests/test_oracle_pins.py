@@ -219,6 +219,23 @@ def test_exact_invariants():
     assert abs(lhs - rhs) < 1e-11 * max(1, abs(rhs))
 
 
+def test_E_is_dO_dot_ddO_minus_alpha_D():
+    """E_i = sum_j P_ij dP~_ij equals dO_i . ddO~_i - alpha_i D_i: dP~ depends on dO
+    only through dP = dO V^T and G = dO U_V^T, and the same sums of P-weighted V and
+    U_V rows make up ddO~.  The oracle forms E from its definition and ddO~ from
+    ddP V + P U_V, so a term dropped from either (G, the -alpha dP correction, the
+    -D shift) breaks the identity.  The Pass 1 kernel forms E' this way instead of
+    reducing P o dP~' over keys."""
+    for causal in (False, True):
+        N, d = 23, 7
+        t = rand_inputs(N, d, seed=43)
+        tau = 0.4
+        out = fo.bob(*args(t), tau, causal=causal)
+        _, _, D = fo.forward(t["Q"], t["K"], t["V"], t["dO"], tau, causal=causal)
+        rhs = np.sum(t["dO"] * out["ddOt"], axis=1) - out["alpha"] * D
+        assert np.abs(out["E"] - rhs).max() < 1e-12 * max(1.0, np.abs(out["E"]).max())
+
+
 def test_softmax_adjoint_rows_sum_to_zero():
     t = rand_inputs(15, 4, seed=51)
     tau = 0.5
@@ -369,6 +386,22 @@ def test_fd_pin_catches_planted_mistakes(monkeypatch, mutation):
     for name, key in (("Q", "dQt"), ("K", "dKt"), ("V", "dVt"), ("dO", "ddOt")):
         worst = max(worst, rel_err(out[key], central_fd(f, t[name])))
     assert worst > 1e-3, f"mutation {mutation} not detected (worst rel err {worst})"
+
+
+@pytest.mark.parametrize("mutation", ["drop_G", "ddP_without_D_path", "alpha_sign", "ddO_drop_PUV"])
+def test_E_identity_catches_planted_mistakes(monkeypatch, mutation):
+    """The identity E = dO . ddO~ - alpha D fails on every planted slip that touches E
+    or ddO~ (a wrong F or a missing tau on dQ~ leaves it intact; the FD pin above
+    catches those)."""
+    N, d = 9, 5
+    t = rand_inputs(N, d, seed=124)
+    tau = 0.45
+    monkeypatch.setattr(fo, "_row_chain", _mutant_bob(mutation))
+    out = fo.bob(*args(t), tau)
+    monkeypatch.undo()
+    _, _, D = fo.forward(t["Q"], t["K"], t["V"], t["dO"], tau)
+    rhs = np.sum(t["dO"] * out["ddOt"], axis=1) - out["alpha"] * D
+    assert np.abs(out["E"] - rhs).max() > 1e-3 * max(1.0, np.abs(out["E"]).max()), mutation
 
 
 @pytest.mark.parametrize("causal", [False, True])
