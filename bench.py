@@ -184,7 +184,8 @@ def max_n_sweep(args):
     """Sweep the sequence length of one long head (B=1 H=1 d=64 bf16, the
     long-context workload's shape) upward by powers of two while the next call
     is predicted (N^2 scaling) to stay under --max-seconds.  Each length runs the
-    forward and one timed BoB call, then checks size-independent properties of
+    forward and one timed BoB call (its two passes issued one after the other with
+    a progress line between them), then checks size-independent properties of
     the outputs: all finite, and the column sums of dK~ and dV~ vanish (Phi is
     invariant under K -> K + 1c^T and V -> V + 1c^T)."""
     import torch
@@ -207,7 +208,14 @@ def max_n_sweep(args):
         O, L, D = fb.forward(T[0], T[1], T[2], T[3], tau)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        out = fb.bob(*T, O, L, D, tau)
+        print(f"[max-n] N={n}: forward {t1 - t0:.3f} s", file=sys.stderr, flush=True)
+        # The two passes fbob_bob launches, issued one by one so that a line is printed
+        # between them (a call at the largest lengths runs for minutes).
+        out = fb.bob_pass1(*T, O, L, D, tau)
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        print(f"[max-n] N={n}: Pass 1 {tp - t1:.3f} s", file=sys.stderr, flush=True)
+        out.update(fb.bob_pass2(*T, L, D, out["alpha"], out["E"], tau))
         torch.cuda.synchronize()
         t2 = time.perf_counter()
         ok = all(bool(torch.isfinite(v).all()) for v in out.values())
