@@ -91,7 +91,7 @@ def test_headline_n16k_two_heads_full_and_sampled_rows():
     U.say(f"[parity] {w.name} heads 0,11: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
     _check_sampled_rows(w, inp, gpu, n_rows=16)
-    _check_invariants(gpu)
+    _check_invariants(gpu, inp)
 
 
 def _check_sampled_rows(w, inp, gpu, n_rows):
@@ -112,10 +112,12 @@ def _check_sampled_rows(w, inp, gpu, n_rows):
     assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
 
 
-def _check_invariants(gpu):
+def _check_invariants(gpu, inp):
     """Column sums of dK~ and dV~ vanish exactly (Phi is invariant under K -> K + 1c^T
     and V -> V + 1c^T); with per-element rounding the sum over N keys is tiny
-    compared with the sum of magnitudes."""
+    compared with the sum of magnitudes.  And at every row E = dO . ddO~ - alpha D
+    (dP~ depends on dO only through dP and G): Pass 1 forms E by a reduction over
+    keys, so this ties it to ddO~, alpha and D where the oracle only samples rows."""
     for key in ("dKt", "dVt"):
         x = gpu[key]
         s = np.abs(x.sum(axis=2))
@@ -123,6 +125,10 @@ def _check_invariants(gpu):
         ratio = float(np.max(s / np.maximum(m, 1e-30)))
         U.say(f"[parity] invariant sum_j {key}: max ratio {ratio:.2e}")
         assert ratio < 1e-2, (key, ratio)
+    rhs = np.einsum("bhnd,bhnd->bhn", inp["dO"].astype(np.float64), gpu["ddOt"]) - gpu["alpha"] * gpu["D"]
+    err = U.rel(gpu["E"], rhs)
+    U.say(f"[parity] invariant E = dO . ddO~ - alpha D: {err:.2e}")
+    assert err < 2e-2, err
 
 
 @pytest.mark.parametrize("name", ["h8_n65536_d128_bf16_qk2", "h1_n262144_d64_bf16"])
@@ -132,7 +138,7 @@ def test_large_sampled_rows_and_invariants(name):
     inp = U.make_inputs(w)
     gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
     _check_sampled_rows(w, inp, gpu, n_rows=8 if w.H > 1 else 32)
-    _check_invariants(gpu)
+    _check_invariants(gpu, inp)
 
 
 @pytest.mark.parametrize("name", ["pages_causal_b4_h12_n16384_d64_bf16",
@@ -151,7 +157,7 @@ def test_pages_causal_shape_full_two_heads(name):
           + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
     _check_sampled_rows(w, inp, gpu, n_rows=4)
-    _check_invariants(gpu)
+    _check_invariants(gpu, inp)
 
 
 def test_bitwise_deterministic():
@@ -237,7 +243,7 @@ def test_n1m_single_head_sampled_rows_and_invariants():
     inp = U.make_inputs(w)
     gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
     _check_sampled_rows(w, inp, gpu, n_rows=8)
-    _check_invariants(gpu)
+    _check_invariants(gpu, inp)
 
 
 # Every compiled Pass 1 / Pass 2 variant that an environment override can select
