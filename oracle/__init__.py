@@ -33,4 +33,6 @@ from .fbob_oracle import (  # noqa: F401
     bob_row_block,
     bob_blocked,
     bob_columns,
+    row_scalars,
+    bob_columns_at,
 )

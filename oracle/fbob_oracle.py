@@ -319,3 +319,61 @@ def bob_columns(Q, K, V, dO, UQ, UK, UV, tau, cols, causal=False, row_block=1024
         dKt += tau * (r["dSt"][:, cols].T @ Q[rows] + r["dS"][:, cols].T @ UQ[rows])
         dVt += r["ddP"][:, cols].T @ dO[rows]
     return dict(dKt=dKt, dVt=dVt)
+
+
+def row_scalars(Q, K, V, dO, UQ, UK, UV, tau, rows, causal=False):
+    """L, D, alpha and E of the selected full-width rows, from the score-shaped
+    blocks S, dP, F, G alone (no d-wide contraction of P-shaped matrices).
+
+    The same definitions as ``_row_chain`` (FlashAttention blog, section 一, for L
+    and D = sum_j P_ij dP_ij over all columns; FlashBoB notes, "关键设计" 1, for
+    alpha and E = sum_j P_ij dP~_ij), evaluated for ``rows`` only.  Cost
+    10 len(rows) N d: five products with every key.  These four per-row numbers
+    are all that a column of dK~ or dV~ needs from a row (``bob_columns_at``).
+    """
+    rows = np.asarray(rows)
+    Q, K, V, dO, UQ, UK, UV = map(_f64, (Q, K, V, dO, UQ, UK, UV))
+    Qr, dOr, UQr = Q[rows], dO[rows], UQ[rows]
+    S = _scores(Qr, K, tau, rows, causal)
+    L = _logsumexp_rows(S)
+    P = np.exp(S - _col(L))
+    dP = dOr @ V.T
+    D = _rowsum(P * dP)
+    F = tau * (UQr @ K.T + Qr @ UK.T)
+    G = dOr @ UV.T
+    alpha = _rowsum(P * F)
+    dPt = F * (dP - _col(D)) + G - _col(alpha) * dP
+    E = _rowsum(P * dPt)
+    return dict(L=L, D=D, alpha=alpha, E=E)
+
+
+def bob_columns_at(Q, K, V, dO, UQ, UK, UV, tau, cols, L, D, alpha, E, causal=False):
+    """dK~ and dV~ at the selected key positions, given every row's L, D, alpha, E.
+
+    Column j needs, for every row i, P_ij, dP_ij, F_ij and G_ij (products of row i
+    with key j) and the row's four scalars; then, as in ``bob``,
+      dS = P o (dP - D),  dP~ = F o (dP - D) + G - alpha dP,  dS~ = P o (dP~ - E),
+      ddP = P o (F - alpha),  dK~_j = tau sum_i (dS~_ij Q_i + dS_ij U_Q,i),
+      dV~_j = sum_i ddP_ij dO_i.
+    The row scalars must be the oracle's own (``row_scalars`` over all rows).
+    Cost O(N len(cols) d).
+    """
+    cols = np.asarray(cols)
+    Q, K, V, dO, UQ, UK, UV = map(_f64, (Q, K, V, dO, UQ, UK, UV))
+    L, D, alpha, E = map(_f64, (L, D, alpha, E))
+    N = Q.shape[0]
+    Kc, Vc, UKc, UVc = K[cols], V[cols], UK[cols], UV[cols]
+    S = tau * (Q @ Kc.T)                                   # (N, c): rows i, columns j
+    P = np.exp(S - _col(L))
+    if causal:
+        P = np.where(cols[None, :] > np.arange(N)[:, None], 0.0, P)
+    dP = dO @ Vc.T
+    F = tau * (UQ @ Kc.T + Q @ UKc.T)
+    G = dO @ UVc.T
+    dS = P * (dP - _col(D))
+    dPt = F * (dP - _col(D)) + G - _col(alpha) * dP
+    dSt = P * (dPt - _col(E))
+    ddP = P * (F - _col(alpha))
+    dKt = tau * (dSt.T @ Q + dS.T @ UQ)
+    dVt = ddP.T @ dO
+    return dict(dKt=dKt, dVt=dVt)

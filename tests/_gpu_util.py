@@ -44,6 +44,46 @@ def run_gpu(dev: dict, tau: float, causal: bool):
     return res
 
 
+def class_tiled_errors(B, H, N, d, dtype, p, seed, tau):
+    """Run forward + BoB on class-tiled inputs (workloads.class_tiled: every row a
+    copy of one of p class rows, each class used N / p times) and compare EVERY
+    element of every output with the fp64 oracle on the p class rows, gathered by
+    class (L shifted by ln(N / p)): the reduction pinned on the CPU by
+    test_class_tiled_inputs_reduce_to_the_small_problem.  Comparison on the device
+    in float64.  Returns {output: max|gpu - ref| / max|ref|}."""
+    import math
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    small, sigma = workloads.class_tiled(B, H, N, d, dtype, p, seed)
+    dev = torch.device("cuda")
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    sig = torch.from_numpy(sigma).to(dev)
+    full = {k: torch.from_numpy(v).to(dev).index_select(2, sig).to(td).contiguous()
+            for k, v in small.items()}
+    O, L, D = fb.forward(full["Q"], full["K"], full["V"], full["dO"], tau)
+    out = fb.bob(full["Q"], full["K"], full["V"], full["dO"], full["UQ"], full["UK"], full["UV"],
+                 O, L, D, tau)
+    out.update(O=O, L=L, D=D)
+    torch.cuda.synchronize()
+    del full
+    ref = {k: np.zeros((B, H, p) + ((d,) if k in ("dQt", "dKt", "dVt", "ddOt", "O") else ()))
+           for k in out}
+    for b in range(B):
+        for h in range(H):
+            a = [small[k][b, h].astype(np.float64) for k in workloads.TENSORS]
+            r = oracle.bob(*a, tau)
+            O_s, L_s, D_s = oracle.forward(*a[:4], tau)
+            r.update(O=O_s, L=L_s + math.log(N // p), D=D_s)
+            for k in ref:
+                ref[k][b, h] = r[k]
+    errs = {}
+    for k, g in out.items():
+        rf = torch.from_numpy(ref[k]).to(dev).index_select(2, sig)
+        errs[k] = float((g.double() - rf).abs().max() / rf.abs().max())
+        del rf
+    return errs
+
+
 def rel(a, b):
     den = np.max(np.abs(b)) if b.size else 0.0
     if den == 0.0:

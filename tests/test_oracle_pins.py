@@ -315,6 +315,98 @@ def test_rows_blocks_and_columns_agree_with_plain(causal):
         assert rel_err(c[k], full[k][cols]) < 1e-13, k
 
 
+@pytest.mark.parametrize("N,d,causal", [(7, 4, False), (9, 3, True)])
+def test_columns_from_row_scalars_match_fd_of_phi(N, d, causal):
+    """dK~, dV~ at selected key positions from every row's (L, D, alpha, E) are the
+    gradient of Phi with respect to those rows of K and V (central differences;
+    nothing of ``bob`` is used)."""
+    t = rand_inputs(N, d, seed=200 + N)
+    tau = 0.55
+    rs = fo.row_scalars(*args(t), tau, np.arange(N), causal)
+    cols = np.array([0, 2, N - 1])
+    c = fo.bob_columns_at(*args(t), tau, cols, rs["L"], rs["D"], rs["alpha"], rs["E"], causal)
+
+    def f():
+        return fo.phi(*args(t), tau, causal)
+
+    for name, key in (("K", "dKt"), ("V", "dVt")):
+        fd = central_fd(f, t[name])[cols]
+        assert rel_err(c[key], fd) < 1e-7, (name, rel_err(c[key], fd))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_scalars_and_columns_agree_with_plain(causal):
+    """The row-scalar pass equals the forward's L, D and the plain BoB's alpha, E; the
+    columns built from it equal the plain BoB's dK~, dV~, and summed over all keys
+    they vanish (Phi is invariant under K -> K + 1c^T and V -> V + 1c^T)."""
+    N, d = 70, 8
+    t = rand_inputs(N, d, seed=92)
+    tau = 1 / math.sqrt(d)
+    full = fo.bob(*args(t), tau, causal)
+    _, L, D = fo.forward(t["Q"], t["K"], t["V"], t["dO"], tau, causal)
+    rs = {k: np.empty(N) for k in ("L", "D", "alpha", "E")}
+    for r0 in range(0, N, 16):  # row blocks: rows are independent
+        rows = np.arange(r0, min(N, r0 + 16))
+        part = fo.row_scalars(*args(t), tau, rows, causal)
+        for k in rs:
+            rs[k][rows] = part[k]
+    np.testing.assert_allclose(rs["L"], L, rtol=1e-14)
+    np.testing.assert_allclose(rs["D"], D, rtol=1e-12, atol=1e-13)
+    for k in ("alpha", "E"):
+        assert rel_err(rs[k], full[k]) < 1e-13, k
+    allc = fo.bob_columns_at(*args(t), tau, np.arange(N), rs["L"], rs["D"], rs["alpha"],
+                             rs["E"], causal)
+    for k in ("dKt", "dVt"):
+        assert rel_err(allc[k], full[k]) < 1e-12, k
+        assert np.abs(allc[k].sum(axis=0)).max() < 1e-12 * np.abs(allc[k]).sum()
+    cols = np.array([1, 5, 64, 69])
+    c = fo.bob_columns_at(*args(t), tau, cols, rs["L"], rs["D"], rs["alpha"], rs["E"], causal)
+    for k in ("dKt", "dVt"):
+        assert rel_err(c[k], full[k][cols]) < 1e-12, k
+
+
+@pytest.mark.parametrize("which", ["L", "D", "alpha", "E"])
+def test_columns_depend_on_each_row_scalar(which):
+    """A slip in any of the four row scalars handed to the column evaluation (here a
+    shift of 0.05 in one of them) moves dK~ or dV~ well past the FD pin's bound, so
+    that pin sees each scalar's role."""
+    N, d = 8, 4
+    t = rand_inputs(N, d, seed=301)
+    tau = 0.5
+    rs = fo.row_scalars(*args(t), tau, np.arange(N))
+    bad = dict(rs)
+    bad[which] = rs[which] + 0.05
+    good = fo.bob_columns_at(*args(t), tau, np.arange(N), **rs)
+    off = fo.bob_columns_at(*args(t), tau, np.arange(N), **bad)
+    worst = max(rel_err(off[k], good[k]) for k in ("dKt", "dVt"))
+    assert worst > 1e-3, (which, worst)
+
+
+@pytest.mark.parametrize("p_rows,m", [(7, 5), (4, 9)])
+def test_class_tiled_inputs_reduce_to_the_small_problem(p_rows, m):
+    """If the N = m p rows of every input are copies of p class rows, each class used
+    m times, then P_ij = P~_ab / m for classes a, b of i, j, and every BoB output (and
+    O, D) of the full problem equals the p-row problem's output of the class, while
+    L rises by ln m.  This lets a full-size GPU result be checked element by element
+    against the oracle on the p class rows."""
+    import workloads
+    N, d = m * p_rows, 4
+    small, sigma = workloads.class_tiled(1, 1, N, d, "f32", p_rows, seed=17)
+    sm = {k: v[0, 0].astype(np.float64) for k, v in small.items()}
+    full = {k: v[sigma] for k, v in sm.items()}
+    assert sorted(np.bincount(sigma)) == [m] * p_rows
+    tau = 0.7
+    a_s = [sm[k] for k in ("Q", "K", "V", "dO", "UQ", "UK", "UV")]
+    a_f = [full[k] for k in ("Q", "K", "V", "dO", "UQ", "UK", "UV")]
+    ref, got = fo.bob(*a_s, tau), fo.bob(*a_f, tau)
+    for k in OUT4 + ("alpha", "E"):
+        assert rel_err(got[k], ref[k][sigma]) < 1e-12, k
+    O_s, L_s, D_s = fo.forward(*a_s[:4], tau)
+    O_f, L_f, D_f = fo.forward(*a_f[:4], tau)
+    assert rel_err(O_f, O_s[sigma]) < 1e-13 and rel_err(D_f, D_s[sigma]) < 1e-12
+    np.testing.assert_allclose(L_f, L_s[sigma] + math.log(m), rtol=1e-14)
+
+
 def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3, 1.0 + 2 ** -8 + 2 ** -20],
                  dtype=np.float32)
@@ -457,7 +549,8 @@ def test_first_backward_column_sums():
 def test_oracle_package_exports():
     for name in ("forward", "first_backward", "first_backward_rows", "first_backward_blocked",
                  "phi", "bob", "bob_affine", "bob_rows", "hvp_half_squared_output",
-                 "bob_blocked", "bob_columns", "attention_probs"):
+                 "bob_blocked", "bob_columns", "attention_probs", "row_scalars",
+                 "bob_columns_at"):
         assert callable(getattr(oracle, name))
 
 

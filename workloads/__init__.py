@@ -13,6 +13,7 @@ Recipe (one per workload, fixed order Q, K, V, dO, U_Q, U_K, U_V):
 
 from __future__ import annotations
 
+import hashlib
 import math
 from dataclasses import dataclass, field
 
@@ -121,7 +122,62 @@ def make_inputs(w: Workload, heads=None) -> dict:
     return out
 
 
+def make_inputs_device(w: Workload, device="cuda"):
+    """The seven inputs of ``w`` drawn directly on a GPU, for lengths where a host
+    draw and upload would dominate (the long-head sweep): torch's device generator
+    seeded with ``w.seed``, ``randn`` in float32 per tensor in the fixed order, the
+    same scalings, then rounding to the storage type (torch's float32 -> bfloat16
+    conversion rounds to nearest even).  A different stream of numbers from
+    ``make_inputs``; both sides of a comparison use the returned tensors.
+    Returns {name: tensor [B, H, N, d]} in the storage dtype.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {}
+    for name in TENSORS:
+        t = torch.randn((w.B, w.H, w.N, w.d), generator=g, device=device, dtype=torch.float32)
+        if name in ("UQ", "UK", "UV") and w.scale_u != 1.0:
+            t *= w.scale_u
+        if name in ("Q", "K") and w.scale_qk != 1.0:
+            t *= w.scale_qk
+        out[name] = t.to(td).contiguous()
+    return out
+
+
+def class_tiled(B: int, H: int, N: int, d: int, dtype: str, p: int, seed: int):
+    """Inputs whose N rows are copies of p seeded "class" rows, every class used
+    exactly N / p times (p must divide N), in a seeded random order.
+
+    Returns (small, sigma): ``small`` holds the seven [B, H, p, d] float32 class
+    tensors (same recipe as make_inputs: i.i.d. N(0,1), bf16-rounded for bf16), and
+    ``sigma`` the length-N int64 class of each position, sigma = perm(N) mod p, so
+    that the full tensor is small[..., sigma, :].  A random order (not i mod p)
+    makes a row read from the wrong address land in a different class.
+    """
+    if N % p:
+        raise ValueError("p must divide N")
+    w = Workload("class_rows", B=B, H=H, N=p, d=d, dtype=dtype, seed=seed)
+    small_inp = make_inputs(w)
+    perm = np.random.Generator(np.random.PCG64(seed + 1)).permutation(N)
+    return small_inp, (perm % p).astype(np.int64)
+
+
 def small(name: str, B: int, H: int, N: int, d: int, dtype: str, seed: int,
           **kw) -> Workload:
     """An ad-hoc workload with the same recipe (used for edge-case and tail tests)."""
     return Workload(name, B=B, H=H, N=N, d=d, dtype=dtype, seed=seed, **kw)
+
+
+def input_digest(inp: dict, heads) -> str:
+    """SHA-256 over the float32 values of the given flat (b*H + h) heads of every
+    tensor in ``inp``, tensors in draw order: identifies a seeded draw, e.g. to
+    check that stored expected values were computed from the same inputs."""
+    h = hashlib.sha256()
+    for name in TENSORS:
+        x = inp[name]
+        x = x.reshape(-1, x.shape[-2], x.shape[-1])
+        for f in heads:
+            h.update(np.ascontiguousarray(x[f], dtype=np.float32).tobytes())
+    return h.hexdigest()
