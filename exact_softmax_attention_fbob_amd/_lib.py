@@ -6,6 +6,7 @@ fallback implementation.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -38,6 +39,24 @@ class FbobError(RuntimeError):
         except Exception:  # pragma: no cover - message only
             pass
         super().__init__(msg)
+
+
+def tuning_library_path() -> str:
+    """The measurement build (variants selectable by FBOB_TUNE_* variables)."""
+    return os.path.join(_HERE, "libfbob_tuning.so")
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route the binding's calls through another build of the same C ABI (e.g. the
+    measurement build) inside the ``with`` block."""
+    global _LIB
+    prev = _LIB
+    _LIB = load_library(path)
+    try:
+        yield _LIB
+    finally:
+        _LIB = prev
 
 
 def load_library(path: str | None = None):

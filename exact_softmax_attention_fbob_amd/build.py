@@ -1,6 +1,13 @@
-"""Build the gfx950 HIP library ``libfbob.so`` in-tree (next to this file).
+"""Build the gfx950 HIP libraries in-tree (next to this file).
 
-    python -m exact_softmax_attention_fbob_amd.build [--verbose]
+    python -m exact_softmax_attention_fbob_amd.build [--verbose] [--product-only]
+
+* ``libfbob.so``: the product library.  One kernel variant per problem class; it
+  reads no environment.
+* ``libfbob_tuning.so``: the same sources with ``-DFBOB_TUNING=1``, which also
+  compiles the measured alternative variants and lets ``FBOB_TUNE_<KERNEL>``
+  environment variables select one at each launch (measurement and the variant
+  parity tests only).
 
 hipcc cross-compiles for gfx950 without a GPU present.  Packed fp32 VALU
 instructions are disabled in device code (``-packed-fp32-ops``); hipcc's host
@@ -18,6 +25,7 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfbob.so")
+TUNING_LIB = os.path.join(HERE, "libfbob_tuning.so")
 SOURCES = ("fbob_api.hip", "fbob_forward.hip", "fbob_pass1.hip", "fbob_pass2.hip",
            "fbob_grad.hip")
 ARCH = "gfx950"
@@ -36,10 +44,14 @@ def flags(extra=()):
             "-Wno-unused-command-line-argument", *extra]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every source to an object in parallel, then link libfbob.so."""
+def build(verbose: bool = False, extra=(), tuning: bool = False) -> str:
+    """Compile every source to an object in parallel, then link libfbob.so (or,
+    with ``tuning``, libfbob_tuning.so)."""
     cc = hipcc()
-    objdir = os.path.join(HERE, "_build")
+    lib = TUNING_LIB if tuning else LIB
+    if tuning:
+        extra = (*extra, "-DFBOB_TUNING=1")
+    objdir = os.path.join(HERE, "_build_tuning" if tuning else "_build")
     os.makedirs(objdir, exist_ok=True)
     t0 = time.time()
     procs = []
@@ -61,16 +73,25 @@ def build(verbose: bool = False, extra=()) -> str:
             sys.stderr.write(out + "\n")
     if failed:
         raise RuntimeError(f"HIP build failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(link)}\n{r.stdout}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        sys.stderr.write(f"[fbob build] {LIB} in {time.time() - t0:.1f}s\n")
-    return LIB
+        sys.stderr.write(f"[fbob build] {lib} in {time.time() - t0:.1f}s\n")
+    return lib
+
+
+def build_all(verbose: bool = False) -> None:
+    """Both libraries, one after the other (each compiles its sources in parallel)."""
+    build(verbose=verbose)
+    build(verbose=verbose, tuning=True)
 
 
 if __name__ == "__main__":
-    build(verbose="--verbose" in sys.argv)
+    if "--product-only" in sys.argv:
+        build(verbose="--verbose" in sys.argv)
+    else:
+        build_all(verbose="--verbose" in sys.argv)

@@ -15,7 +15,6 @@
 // maximum exceeds it by more than kSlack (weights then stay <= 2^kSlack), so the
 // accumulator rescale is rare.  The row sum of the weights is an MFMA contraction
 // with a ones operand over the same bf16 weights that multiply V.
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -244,11 +243,12 @@ hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
       if (tau_is_pow2(p.tau)) {
         // 128-key stages and raised wave priority over the P V MFMAs; 1 selects 16
         // rows per wave, 2 64-key stages, 3 the plain instruction order.
-        const char* v = getenv("FBOB_TUNE_FWD");
-        const int cfg = v ? atoi(v) : 0;
+#if FBOB_TUNING
+        const int cfg = tune_choice("FBOB_TUNE_FWD");
         if (cfg == 1) return launch_t<__bf16, 64, 8, 64, true, true, 1>(p, a, s);
         if (cfg == 2) return launch_t<__bf16, 64, 8, 64, true, true, 2>(p, a, s);
         if (cfg == 3) return launch_t<__bf16, 64, 8, 128, true, false, 2>(p, a, s);
+#endif
         return launch_t<__bf16, 64, 8, 128, true, true, 2>(p, a, s);
       }
       return launch_t<__bf16, 64, 8, 128, false, false, 2>(p, a, s);
@@ -256,13 +256,14 @@ hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
     // d = 128: 64-key stages; 1 and 2 select 16 rows per wave with 32-key stages
     // and 8 or 4 waves per work-group, 3 16 rows per wave with 64-key stages, 4
     // raised priority over the P V MFMAs, 5 128-key stages.
-    const char* v = getenv("FBOB_TUNE_FWD_D128");
-    const int cfg = v ? atoi(v) : 0;
+#if FBOB_TUNING
+    const int cfg = tune_choice("FBOB_TUNE_FWD_D128");
     if (cfg == 1) return launch_t<__bf16, 128, 8, 32, false>(p, a, s);
     if (cfg == 2) return launch_t<__bf16, 128, 4, 32, false>(p, a, s);
     if (cfg == 3) return launch_t<__bf16, 128, 8, 64, false>(p, a, s);
     if (cfg == 4) return launch_t<__bf16, 128, 8, 64, false, true, 2>(p, a, s);
     if (cfg == 5) return launch_t<__bf16, 128, 8, 128, false, false, 2>(p, a, s);
+#endif
     return launch_t<__bf16, 128, 8, 64, false, false, 2>(p, a, s);
   }
   if (p.d == 64) return launch_t<float, 64, 4, 32, false>(p, a, s);

@@ -15,7 +15,6 @@
 // the contracted index on the MFMA row axis so that their C registers are the B
 // operand of the following contraction, dP - D obtained by seeding the dP
 // accumulator with -D, staged tiles read back with the swizzled LDS readers.
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -422,15 +421,20 @@ hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s) {
   if (p.bf16) {
     // 32 query rows per wave (~3-5 % faster than 16 on the whole backward); 1
     // selects 16 rows per wave, 2 the other stage size.
-    const char* v = getenv(p.d == 64 ? "FBOB_TUNE_DQ" : "FBOB_TUNE_DQ_D128");
-    const int cfg = v ? atoi(v) : 0;
+#if FBOB_TUNING
+    const int cfg = tune_choice(p.d == 64 ? "FBOB_TUNE_DQ" : "FBOB_TUNE_DQ_D128");
+#endif
     if (p.d == 64) {
+#if FBOB_TUNING
       if (cfg == 1) return launch_dq<__bf16, 64, 8, 64, true, 1>(p, a, s);
       if (cfg == 2) return launch_dq<__bf16, 64, 8, 64, true, 2>(p, a, s);
+#endif
       return launch_dq<__bf16, 64, 8, 128, true, 2>(p, a, s);
     }
+#if FBOB_TUNING
     if (cfg == 1) return launch_dq<__bf16, 128, 8, 32, true, 1>(p, a, s);
     if (cfg == 2) return launch_dq<__bf16, 128, 8, 32, true, 2>(p, a, s);
+#endif
     return launch_dq<__bf16, 128, 8, 64, true, 2>(p, a, s);
   }
   if (p.d == 64) return launch_dq<float, 64, 4, 32, false>(p, a, s);

@@ -6,7 +6,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Kernel variants.  The shipped library (built without FBOB_TUNING) launches one
+// fixed variant per problem class, compiles no other and reads no environment.  A
+// measurement build (-DFBOB_TUNING=1, libfbob_tuning.so) also compiles the
+// alternatives that were measured against it and lets an environment variable
+// FBOB_TUNE_<KERNEL> pick one at each launch (0 = the shipped variant).
+#ifndef FBOB_TUNING
+#define FBOB_TUNING 0
+#endif
+#if FBOB_TUNING
+#include <stdlib.h>
+#endif
+
 namespace fbob {
+
+#if FBOB_TUNING
+inline int tune_choice(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+#endif
 
 struct Problem {
   int B, Hq, Hkv, N, d;

@@ -31,8 +31,6 @@
 // keeping the operands unscaled (tau applied to the F tile on the VALU), taking
 // the row sums as lane-local fp32 sums, and keeping one LDS offset per access
 // pattern.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "fbob_device.hpp"
@@ -428,24 +426,21 @@ hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int tune_choice(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-
 }  // namespace
 
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.bf16) {
     if (p.d == 64) {
-      const int cfg = tune_choice("FBOB_TUNE_P1");
       if (tau_is_pow2(p.tau)) {
+#if FBOB_TUNING
+        const int cfg = tune_choice("FBOB_TUNE_P1");
         if (cfg == 1) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 64, true>(p, a, s);
         if (cfg == 2) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 32, true>(p, a, s);
         if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 1, kTauPow2, 32, false>(p, a, s);
         if (cfg == 4) return launch_t<__bf16, 64, 8, 1, 0, kTauPow2, 64, true>(p, a, s);
         if (cfg == 5) return launch_t<__bf16, 64, 8, 1, 2, kTauPow2, 64, true>(p, a, s);
         if (cfg == 6) return launch_t<__bf16, 64, 8, 1, 4, kTauPow2, 64, true>(p, a, s);
+#endif
         return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
       }
       return launch_t<__bf16, 64, 8, 1, true, kTauValu, 64, true>(p, a, s);
@@ -454,9 +449,11 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
     // sums and the XOR-form LDS offsets to fit 256 registers; 32-key stages (64-key
     // stages spill).  Alternatives: 1 no scheduling fences, 2 the one-wave-per-SIMD
     // layout with tau-scaled operand copies.
+#if FBOB_TUNING
     const int cfg = tune_choice("FBOB_TUNE_P1_D128");
     if (cfg == 1) return launch_t<__bf16, 128, 8, 1, false, kTauValu, 32, true>(p, a, s);
     if (cfg == 2) return launch_t<__bf16, 128, 4, 1, true, kTauScaled>(p, a, s);
+#endif
     return launch_t<__bf16, 128, 8, 1, true, kTauValu, 32, true>(p, a, s);
   }
   if (p.d == 64) return launch_t<float, 64, 4, 1, true, kTauScaled>(p, a, s);

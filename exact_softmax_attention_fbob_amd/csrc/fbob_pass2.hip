@@ -28,8 +28,6 @@
 // index on the MFMA row axis, so a lane owns one key and four consecutive rows
 // per block; those C registers are directly the B operand of the contractions
 // over rows, whose A operand (Q^T, U_Q^T, dO^T) comes from transposed LDS reads.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "fbob_device.hpp"
@@ -303,23 +301,20 @@ hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int tune_choice(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-
 }  // namespace
 
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
   if (p.bf16) {
     if (p.d == 64) {
-      const int cfg = tune_choice("FBOB_TUNE_P2");
       if (tau_is_pow2(p.tau)) {
+#if FBOB_TUNING
+        const int cfg = tune_choice("FBOB_TUNE_P2");
         if (cfg == 1) return launch_t<__bf16, 64, 8, 2, 64, false, kTauPow2, false>(p, a, s);
         if (cfg == 2) return launch_t<__bf16, 64, 8, 2, 64, true, kTauPow2, true>(p, a, s);
         if (cfg == 3) return launch_t<__bf16, 64, 8, 1, 64, true, kTauPow2, false>(p, a, s);
         if (cfg == 4) return launch_t<__bf16, 64, 8, 2, 64, 3, kTauPow2, true>(p, a, s);
         if (cfg == 5) return launch_t<__bf16, 64, 8, 2, 64, 0, kTauPow2, true>(p, a, s);
+#endif
         return launch_t<__bf16, 64, 8, 2, 64, 4, kTauPow2, true>(p, a, s);
       }
       return launch_t<__bf16, 64, 8, 2, 64, false, kTauValu, true>(p, a, s);
@@ -327,10 +322,12 @@ hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
     // d = 128: unscaled operands (kTauValu) for two waves per SIMD, 64-row stages.
     // Alternatives: 1 with scheduling fences, 2 the one-wave-per-SIMD layout with
     // tau-scaled operand copies, 3 32-row stages.
+#if FBOB_TUNING
     const int cfg = tune_choice("FBOB_TUNE_P2_D128");
     if (cfg == 1) return launch_t<__bf16, 128, 8, 1, 64, true, kTauValu, true>(p, a, s);
     if (cfg == 2) return launch_t<__bf16, 128, 4, 1, 32, true, kTauScaled>(p, a, s);
     if (cfg == 3) return launch_t<__bf16, 128, 8, 1, 32, true, kTauValu, true>(p, a, s);
+#endif
     return launch_t<__bf16, 128, 8, 1, 64, false, kTauValu, true>(p, a, s);
   }
   if (p.d == 64) return launch_t<float, 64, 4, 1, 32, true, kTauScaled>(p, a, s);

@@ -102,7 +102,7 @@ DQ_VARIANTS = [("FBOB_TUNE_DQ", v) for v in (1, 2)] + [("FBOB_TUNE_DQ_D128", v) 
 
 
 @pytest.mark.parametrize("var,val", DQ_VARIANTS, ids=[f"{a}={b}" for a, b in DQ_VARIANTS])
-def test_backward_row_pass_variants(var, val, monkeypatch):
+def test_backward_row_pass_variants(var, val, monkeypatch, tuning_library):
     """Every compiled layout of the row pass (rows per wave, stage size) against the
     oracle, on a ragged tail and on a causal grouped-query case."""
     d = 128 if var.endswith("D128") else 64
