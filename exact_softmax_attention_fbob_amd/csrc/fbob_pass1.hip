@@ -440,6 +440,11 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
         if (cfg == 4) return launch_t<__bf16, 64, 8, 1, 0, kTauPow2, 64, true>(p, a, s);
         if (cfg == 5) return launch_t<__bf16, 64, 8, 1, 2, kTauPow2, 64, true>(p, a, s);
         if (cfg == 6) return launch_t<__bf16, 64, 8, 1, 4, kTauPow2, 64, true>(p, a, s);
+        // one wave per SIMD with 32 query rows (K/V fragments shared by two row
+        // blocks), compiler order, pinned order, pinned order + priority
+        if (cfg == 7) return launch_t<__bf16, 64, 4, 2, 0, kTauPow2, 64, true>(p, a, s);
+        if (cfg == 8) return launch_t<__bf16, 64, 4, 2, 2, kTauPow2, 64, true>(p, a, s);
+        if (cfg == 9) return launch_t<__bf16, 64, 4, 2, 3, kTauPow2, 64, true>(p, a, s);
 #endif
         return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
       }
