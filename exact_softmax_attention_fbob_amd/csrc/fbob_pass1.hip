@@ -44,7 +44,10 @@ namespace {
 // of the MFMAs that use them, with the order pinned by sched_group_barrier; 3 is 2
 // with raised wave priority over the contraction MFMAs, 4 also over the score
 // MFMAs.
-template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT, bool CAUSAL>
+// VSUM: the row sums alpha, E' as lane-local fp32 sums of the unrounded products
+// (the d = 128 and multi-row-block layouts always do this).
+template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT, bool CAUSAL,
+          bool VSUM = false>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     // At d = 128 the registers of the two ones operands are worth more than the VALU
     // adds: there the row sums are lane-local fp32 partial sums (keys 4 g + q of row
     // r), reduced over the four lanes of a row at the end.
-    constexpr bool kVsum = D >= 128 || NI >= 2;
+    constexpr bool kVsum = D >= 128 || NI >= 2 || VSUM;
     float asum[NI], esum[NI];
 
     f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
@@ -409,7 +412,8 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   }
 }
 
-template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC = 32, bool DIRECT = false>
+template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC = 32, bool DIRECT = false,
+          bool VSUM = false>
 hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
@@ -418,10 +422,10 @@ hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   const int total = n_units * p.B * p.Hq;
   const int group = p.Hq / p.Hkv;
   if (p.causal)
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true>), dim3(total), dim3(NW * 64), 0, s,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true, VSUM>), dim3(total), dim3(NW * 64), 0, s,
                        a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   else
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false>), dim3(total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false, VSUM>), dim3(total), dim3(NW * 64), 0,
                        s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
   return hipGetLastError();
 }
@@ -445,6 +449,8 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
         if (cfg == 7) return launch_t<__bf16, 64, 4, 2, 0, kTauPow2, 64, true>(p, a, s);
         if (cfg == 8) return launch_t<__bf16, 64, 4, 2, 2, kTauPow2, 64, true>(p, a, s);
         if (cfg == 9) return launch_t<__bf16, 64, 4, 2, 3, kTauPow2, 64, true>(p, a, s);
+        // the default with alpha, E' as fp32 lane sums of the unrounded products
+        if (cfg == 10) return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true, true>(p, a, s);
 #endif
         return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
       }
