@@ -419,6 +419,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the first-order backward and the autograd HVP step")
+    ap.add_argument("--workspace", action="store_true",
+                    help="time the BoB as one fbob_bob_ws call with a workspace (small "
+                         "problems split their sweeps); per-pass times are then not reported")
     ap.add_argument("--max-n", action="store_true",
                     help="sweep N for one long head instead of the headline step")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
@@ -485,6 +488,9 @@ def main():
         if st != 0:
             raise fb.FbobError(st)
 
+    ws_bytes = fb.bob_workspace_size(T["Q"], T["K"], tau, causal) if args.workspace else 0
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -492,6 +498,15 @@ def main():
                                p(O), p(L), p(D), sp))
         if ev is not None:
             ev[1].record(stream)
+        if args.workspace:  # both passes (and any split reductions) in one call
+            check(lib.fbob_bob_ws(dt_code, B, H, Hkv, N, d, ctau, int(causal), *map(p, qargs),
+                                  p(O), p(L), p(D), p(out["dQt"]), p(out["dKt"]),
+                                  p(out["dVt"]), p(out["ddOt"]), p(out["alpha"]), p(out["E"]),
+                                  p(ws), ws.numel(), sp))
+            if ev is not None:
+                ev[2].record(stream)
+                ev[3].record(stream)
+            return
         check(lib.fbob_bob_pass1(dt_code, B, H, Hkv, N, d, ctau, int(causal), *map(p, qargs),
                                  p(O), p(L), p(D), p(out["dQt"]), p(out["ddOt"]),
                                  p(out["alpha"]), p(out["E"]), sp))
@@ -544,8 +559,12 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     bob_tflops = (f_p1 + f_p2) / (bob_ms * 1e-3) / 1e12
     step_tflops = (f_fwd + f_p1 + f_p2) / (ms_step * 1e-3) / 1e12
-    p1_tflops = f_p1 / (p1_ms * 1e-3) / 1e12
-    p2_tflops = f_p2 / (p2_ms * 1e-3) / 1e12
+    if args.workspace:  # one call: the roofline is the whole BoB (passes + reductions)
+        p1_tflops = bob_tflops
+        p2_tflops = None
+    else:
+        p1_tflops = f_p1 / (p1_ms * 1e-3) / 1e12
+        p2_tflops = f_p2 / (p2_ms * 1e-3) / 1e12
     # the dense peak scales with the clock: 2.5 PFLOP/s bf16 is quoted at 2.4 GHz
     peak_at_clk = peak * sclk / SPEC_SCLK_MHZ if sclk else None
 
@@ -566,26 +585,29 @@ def main():
                    "tau": tau, "inputs": "i.i.d. N(0,1), PCG64 seed %d" % w.seed,
                    "scale_u": w.scale_u, "scale_qk": w.scale_qk},
         "value_is": "BoB (Pass 1 + Pass 2) TFLOP/s: 38 N^2 d per head over the HIP-event "
-                    "time of the two passes, mean over the timed steps",
+                    "time of the two passes, mean over the timed steps"
+                    + ("; one fbob_bob_ws call with a %d-byte workspace" % ws_bytes
+                       if args.workspace else ""),
         "bob_ms_per_call": round(float(bob_ms), 4),
         "bob_tflops": round(bob_tflops, 2),
         "bob_pct_bf16_peak": round(100 * bob_tflops / PEAK_TFLOPS["bf16"], 2),
         "step_tflops": round(step_tflops, 2),
         "step_what": "forward + Pass 1 + Pass 2 (42 N^2 d per head) over the wall time per step",
-        "kernels_ms": {"fwd_stats": round(float(fwd_ms), 4), "bob_pass1": round(float(p1_ms), 4),
-                       "bob_pass2": round(float(p2_ms), 4)},
+        "kernels_ms": {"fwd_stats": round(float(fwd_ms), 4),
+                       "bob_pass1": None if args.workspace else round(float(p1_ms), 4),
+                       "bob_pass2": None if args.workspace else round(float(p2_ms), 4)},
         "median_ms": {k: round(v, 4) for k, v in med.items()},
         "flop_formula": "per (b,h): forward 4 N^2 d, pass1 22 N^2 d, pass2 16 N^2 d"
                         + ("; causal counts N(N+1)/2 of the N^2 pairs" if causal else ""),
         "peak_mem_mib": peak_mib,
         "roofline": {
-            "kernel": "bob_pass1",
+            "kernel": "bob (fbob_bob_ws)" if args.workspace else "bob_pass1",
             "bound": "mfma",
             "achieved": round(p1_tflops, 2),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(p1_tflops / peak, 4),
-            "traffic": measured_traffic(name, "pass1_kernel"),
+            "traffic": None if args.workspace else measured_traffic(name, "pass1_kernel"),
             "sclk_mhz_measured": round(sclk, 1) if sclk else None,
             "peak_at_measured_sclk": round(peak_at_clk, 1) if sclk else None,
             "frac_at_measured_sclk": round(p1_tflops / peak_at_clk, 4) if sclk else None,
@@ -594,9 +616,10 @@ def main():
                            "median over the second half of a ~1.5 s window of back-to-back "
                            "steps); peak scaled from 2.5 PFLOP/s at 2400 MHz",
         },
-        "pass2": {"achieved": round(p2_tflops, 2), "frac": round(p2_tflops / peak, 4),
-                  "frac_at_measured_sclk": round(p2_tflops / peak_at_clk, 4) if sclk else None,
-                  "traffic": measured_traffic(name, "pass2_kernel")},
+        "pass2": None if args.workspace else {
+            "achieved": round(p2_tflops, 2), "frac": round(p2_tflops / peak, 4),
+            "frac_at_measured_sclk": round(p2_tflops / peak_at_clk, 4) if sclk else None,
+            "traffic": measured_traffic(name, "pass2_kernel")},
         "library": "libfbob.so (one kernel variant per problem class; reads no environment)",
     }
     if not args.no_extras:

@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
     bob(Q, K, V, dO, UQ, UK, UV, O, L, D, ...)     -> dict(dQt, dKt, dVt, ddOt, alpha, E)
     bob_pass1(...)                                  -> dict(dQt, ddOt, alpha, E)
     bob_pass2(..., alpha, E)                        -> dict(dKt, dVt)
+    bob_ws(..., workspace)                          -> as bob; small problems split
+    bob_workspace_size(Q, K, tau, causal)           -> bytes bob_ws can use
 Shapes: Q, dO, U_Q: [B, Hq, N, d]; K, V, U_K, U_V: [B, Hkv, N, d]; L, D, alpha,
 E: [B, Hq, N]; all outputs float32.  ``autograd.attention`` wraps forward,
 backward and bob as a twice-differentiable torch operation.
@@ -26,8 +28,8 @@ import os
 
 from ._lib import FbobError, load_library, STATUS  # noqa: F401
 
-__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "load_library", "FbobError",
-           "library_path", "version"]
+__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "bob_ws",
+           "bob_workspace_size", "load_library", "FbobError", "library_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -214,4 +216,47 @@ def bob_pass2(Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, tau=None, causal=False):
     _call(dev, lib.fbob_bob_pass2, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
           int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(L), _p(D),
           _p(alpha), _p(E), _p(out["dKt"]), _p(out["dVt"]), _stream(dev))
+    return out
+
+
+def bob_workspace_size(Q, K, tau=None, causal=False) -> int:
+    """Bytes of device workspace ``bob_ws`` can use for this problem (C ABI
+    ``fbob_bob_workspace_size``); 0 when the problem fills the GPU unsplit."""
+    lib = load_library()
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    out = ctypes.c_int64(0)
+    st = lib.fbob_bob_workspace_size(_dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+                                     int(bool(causal)), ctypes.byref(out))
+    if st != 0:
+        raise FbobError(st)
+    return int(out.value)
+
+
+def bob_ws(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, workspace=None):
+    """BoB with a caller-owned workspace (C ABI ``fbob_bob_ws``): problems too small to
+    fill the GPU split their sweeps over more work-groups.  ``workspace`` is a
+    contiguous GPU tensor of at least ``bob_workspace_size`` bytes (any dtype); None
+    allocates one with torch.  Returns the same dict as ``bob``."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
+    dev = Q.device
+    _row_state(O, L, D, B, Hq, N, d, dev)
+    need = bob_workspace_size(Q, K, tau, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
+    nbytes = workspace.numel() * workspace.element_size()
+    out = dict(dQt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               dKt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               dVt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               ddOt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               alpha=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+               E=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    _call(dev, lib.fbob_bob_ws, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+          _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
+          _p(out["dQt"]), _p(out["dKt"]), _p(out["dVt"]), _p(out["ddOt"]),
+          _p(out["alpha"]), _p(out["E"]), _p(workspace), nbytes, _stream(dev))
     return out

@@ -27,7 +27,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfbob.so")
 TUNING_LIB = os.path.join(HERE, "libfbob_tuning.so")
 SOURCES = ("fbob_api.hip", "fbob_forward.hip", "fbob_pass1.hip", "fbob_pass2.hip",
-           "fbob_grad.hip")
+           "fbob_grad.hip", "fbob_split.hip")
 ARCH = "gfx950"
 
 

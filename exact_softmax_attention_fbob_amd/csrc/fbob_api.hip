@@ -181,6 +181,45 @@ int fbob_backward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
   return finish(fbob::launch_grad_dkv(c.p, a, s));
 }
 
+int fbob_bob_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                            float tau, int causal, int64_t* bytes) {
+  if (bytes == nullptr) return FBOB_ERR_INVALID_ARG;
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  *bytes = c.empty ? 0 : fbob::split_plan(c.p).bytes();
+  return FBOB_OK;
+}
+
+int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+                int causal, const void* Q, const void* K, const void* V, const void* dO,
+                const void* UQ, const void* UK, const void* UV, const float* O, const float* L,
+                const float* D, float* dQt, float* dKt, float* dVt, float* ddOt, float* alpha,
+                float* E, void* workspace, int64_t workspace_bytes, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (workspace_bytes < 0) return FBOB_ERR_INVALID_ARG;
+  if (c.empty) return FBOB_OK;
+  const fbob::SplitPlan plan = fbob::split_plan(c.p);
+  // The split schedule runs only with a workspace that holds its partial sums;
+  // otherwise this is fbob_bob.
+  const bool split = plan.bytes() > 0 && workspace != nullptr && workspace_bytes >= plan.bytes();
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, O, L, D};
+  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, ob, rb, rb};
+  void* outs[] = {dQt, dKt, dVt, ddOt, alpha, E, workspace};
+  const int64_t outb[] = {ob, kob, kob, ob, rb, rb, plan.bytes()};
+  const int st = check_ptrs(ins, inb, 10, outs, outb, split ? 7 : 6);
+  if (st != FBOB_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  fbob::Pass1Args a1{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E};
+  fbob::Pass2Args a2{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
+  if (split) return finish(fbob::launch_bob_split(c.p, a1, a2, plan, workspace, s));
+  if (fbob::launch_pass1(c.p, a1, s) != hipSuccess) return FBOB_ERR_HIP;
+  return finish(fbob::launch_pass2(c.p, a2, s));
+}
+
 int fbob_bob(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
              int causal, const void* Q, const void* K, const void* V, const void* dO,
              const void* UQ, const void* UK, const void* UV, const float* O, const float* L,

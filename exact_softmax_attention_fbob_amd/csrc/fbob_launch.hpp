@@ -43,13 +43,36 @@ struct Pass1Args {
   const void *Q, *K, *V, *dO, *UQ, *UK, *UV;
   const float *O, *L, *D;
   float *dQt, *ddOt, *alpha, *E;
+  // Split key sweep (small grids): part_acc[s][B Hq][N][4][d] holds the four
+  // accumulators (B, X, Omega, ddO~') of split s, part_rs[s][B Hq][N][2] its alpha
+  // and E' partial sums; split s covers keys s * split_keys .. + split_keys - 1.
+  float *part_acc = nullptr, *part_rs = nullptr;
+  int nsplit = 1, split_keys = 0;
 };
 
 struct Pass2Args {
   const void *Q, *K, *V, *dO, *UQ, *UK, *UV;
   const float *L, *D, *alpha, *E;
   float *dKt, *dVt;
+  // Split row sweep (small grids): part[s][B Hkv][N][2][d] holds tau dK~ and dV~ of
+  // split s, which covers row steps s * split_steps .. + split_steps - 1.
+  float* part = nullptr;
+  int nsplit = 1, split_steps = 0;
 };
+
+// How a BoB call spreads small problems over the GPU: each Pass 1 row tile's key
+// sweep in s1 parts, each Pass 2 column tile's row sweep in s2 parts (1 = no
+// split), and the device workspace the partial sums need.
+struct SplitPlan {
+  int s1 = 1, s2 = 1;
+  int split_keys = 0, split_steps = 0;
+  int64_t bytes1 = 0, bytes2 = 0;  // Pass 1 / Pass 2 partials (the two reuse one buffer)
+  int64_t bytes() const { return bytes1 > bytes2 ? bytes1 : bytes2; }
+};
+SplitPlan split_plan(const Problem& p);
+// Pass 1 in s1 parts + reduction, then Pass 2 in s2 parts + reduction, on `s`.
+hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1, const Pass2Args& a2,
+                            const SplitPlan& plan, void* workspace, hipStream_t s);
 
 // First-order backward: the row pass writes dQ and D, the column pass reads D.
 struct GradArgs {
@@ -60,6 +83,9 @@ struct GradArgs {
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s);
+// The partial-sum forms (a.nsplit > 1) of the default Pass 1 / Pass 2 variants.
+hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t s);
+hipError_t launch_pass2_split(const Problem& p, const Pass2Args& a, hipStream_t s);
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s);
 hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s);
 hipError_t launch_grad_dkv(const Problem& p, const GradArgs& a, hipStream_t s);

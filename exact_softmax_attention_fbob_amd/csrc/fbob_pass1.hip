@@ -46,8 +46,11 @@ namespace {
 // MFMAs.
 // VSUM: the row sums alpha, E' as lane-local fp32 sums of the unrounded products
 // (the d = 128 and multi-row-block layouts always do this).
+// SPLIT (no mask): the work-group sweeps one part of the keys and writes its raw
+// accumulators and row sums to a.part_acc / a.part_rs; a reduction kernel adds the
+// parts and applies the correction.
 template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT, bool CAUSAL,
-          bool VSUM = false>
+          bool VSUM = false, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
                                                         float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
@@ -75,9 +78,13 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   // does not fit the register budget: one tile per work-group, the longest
   // dispatched first.
   constexpr bool kFold = CAUSAL && D < 128;
+  static_assert(!(SPLIT && CAUSAL), "the split sweep is for unmasked problems");
   const int n_units = kFold ? (n_row_tiles + 1) / 2 : n_row_tiles;
-  const int bh = logical / n_units;
-  const int unit = logical % n_units;
+  // SPLIT: the parts of one row tile are consecutive work-groups (one XCD).
+  const int split = SPLIT ? logical % a.nsplit : 0;
+  const int lt = SPLIT ? logical / a.nsplit : logical;
+  const int bh = lt / n_units;
+  const int unit = lt % n_units;
   const int b = bh / Hq, h = bh % Hq, hk = h / group;
   const int64_t q_off = (int64_t)bh * N * D;
   const int64_t kv_off = ((int64_t)b * (Hq / group) + hk) * N * D;
@@ -142,9 +149,10 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     // At d = 128 the lane keeps one LDS offset per access pattern (XOR form).
     const LdsLane<T, D, (D >= 128 || NI >= 2)> rd(r, g);
 
-    int jend = N;
+    const int jbeg = SPLIT ? split * a.split_keys : 0;  // a multiple of kBC
+    int jend = SPLIT ? min(N, jbeg + a.split_keys) : N;
     if (CAUSAL) jend = min(N, rt * kBR + kBR);
-    const int ntc = (jend + kBC - 1) / kBC;
+    const int ntc = max(jend - jbeg + kBC - 1, 0) / kBC;
 
     // Operand fragments of one 32-key tile for the contractions over keys.
     struct Frags {
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       else st.store(buf);
     };
     stage_init();
-    stage_load(lds[0], 0);
+    stage_load(lds[0], jbeg);  // rows are clamped to N - 1 (an empty part computes nothing)
     stage_commit(lds[0]);
     __syncthreads();
 
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     // tile t+1 in `nxt`, barrier.  Unrolled by two so that both LDS buffers are
     // compile-time addresses.
     auto step = [&](int t, char* cur, char* nxt) {
-      const int j0 = t * kBC;
+      const int j0 = jbeg + t * kBC;
       const bool more = t + 1 < ntc;
       if (more) stage_load(nxt, j0 + kBC);
       if (active_tile(t)) compute_stage(cur, j0);
@@ -386,6 +394,26 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       // F carries tau through the scaled resident operands.
       const float al = kVsum ? group_sum(asum[ib]) : __shfl(accAE[ib][0], r);
       const float edeg = kVsum ? group_sum(esum[ib]) : __shfl(accAE[ib][0], 32 + r);
+      if constexpr (SPLIT) {
+        if (i < N) {
+          const int64_t heads = (int64_t)gridDim.x / ((int64_t)n_units * a.nsplit);
+          const int64_t prow = ((int64_t)split * heads + bh) * N + i;
+          float* pa = a.part_acc + prow * 4 * D;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const int d0 = 16 * db + 4 * g;
+            *reinterpret_cast<f32x4*>(pa + d0) = accB[ib][db];
+            *reinterpret_cast<f32x4*>(pa + D + d0) = accX[ib][db];
+            *reinterpret_cast<f32x4*>(pa + 2 * D + d0) = accW[ib][db];
+            *reinterpret_cast<f32x4*>(pa + 3 * D + d0) = accO[ib][db];
+          }
+          if (g == 0) {
+            a.part_rs[2 * prow] = al;
+            a.part_rs[2 * prow + 1] = edeg;
+          }
+        }
+        continue;
+      }
       if (i < N) {
         const int64_t ro = q_off + (int64_t)i * D;
 #pragma unroll
@@ -430,7 +458,25 @@ hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT>
+hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
+  constexpr int kBR = NW * 16 * NI;
+  const int n_row_tiles = (p.N + kBR - 1) / kBR;
+  const int total = n_row_tiles * p.B * p.Hq * a.nsplit;
+  hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false, false, true>),
+                     dim3(total), dim3(NW * 64), 0, s, a, p.Hq, p.Hq / p.Hkv, p.N, p.tau,
+                     n_row_tiles, total);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// The shipped variants of launch_pass1 below (bf16, no mask, d = 64 with tau a power of
+// two, or d = 128), in split form; split_plan admits no other problem.
+hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t s) {
+  if (p.d == 64) return launch_split_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
+  return launch_split_t<__bf16, 128, 8, 1, true, kTauValu, 32, true>(p, a, s);
+}
 
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.bf16) {

@@ -39,9 +39,13 @@ namespace {
 // SCHED: 0 leaves instruction order to the compiler, 1 fences the phases and
 // column blocks; 3 raises the wave priority over the contraction MFMAs, 4 also over
 // the score MFMAs (no fences otherwise).
-template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DIRECT, bool CAUSAL>
+// SPLIT (no mask): the work-group sweeps one part of the row steps and writes tau dK~
+// and dV~ of that part to a.part; a reduction kernel adds the parts.
+template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DIRECT, bool CAUSAL,
+          bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
                                                         float tau, int n_col_tiles, int total) {
+  static_assert(!(SPLIT && CAUSAL), "the split sweep is for unmasked problems");
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr bool FENCE = SCHED == 1;
@@ -66,7 +70,10 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   // key/value heads stay in consecutive work-groups.
   constexpr bool kFold = CAUSAL && D < 128;
   const int n_units = kFold ? (n_col_tiles + 1) / 2 : n_col_tiles;
-  const int bhk = logical / n_units, unit = logical % n_units;
+  // SPLIT: the parts of one column tile are consecutive work-groups (one XCD).
+  const int split = SPLIT ? logical % a.nsplit : 0;
+  const int lt = SPLIT ? logical / a.nsplit : logical;
+  const int bhk = lt / n_units, unit = lt % n_units;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int Hq = Hkv * group;
   const int64_t kv_off = (int64_t)bhk * N * D;
@@ -241,14 +248,21 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       if constexpr (kPrioOut) FBOB_PRIO_LOW();
     };
 
-    load_step(0, lds[0]);
+    // This work-group's row steps (all of them unless SPLIT).
+    const int step_lo = SPLIT ? min(nsteps, split * a.split_steps) : 0;
+    const int step_hi = SPLIT ? min(nsteps, step_lo + a.split_steps) : nsteps;
+    // An empty part (possible when the steps do not divide evenly) stages nothing:
+    // step nsteps would address the query head after the group.  Uniform per
+    // work-group, so the barriers below stay uniform too.
+    if (step_lo < step_hi) {
+    load_step(step_lo, lds[0]);
     if constexpr (DIRECT) wait_all_memory();
     store_step(lds[0]);
     __syncthreads();
 
     auto step = [&](int t, char* cur, char* nxt) {
       const int i0 = i_begin + (t % nrc) * BRS;
-      const bool more = t + 1 < nsteps;
+      const bool more = t + 1 < step_hi;
       if (more) load_step(t + 1, nxt);
 #pragma unroll
       for (int sc = 0; sc < BRS / 32; ++sc) {
@@ -262,16 +276,27 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       __syncthreads();
     };
 #pragma unroll 1
-    for (int t = 0; t < nsteps; t += 2) {
+    for (int t = step_lo; t < step_hi; t += 2) {
       step(t, lds[0], lds[1]);
-      if (t + 1 < nsteps) step(t + 1, lds[1], lds[0]);
+      if (t + 1 < step_hi) step(t + 1, lds[1], lds[0]);
     }
+    }  // step_lo < step_hi
 
     // ---- single exclusive write of dK~ and dV~ ----
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
       const int j = jw0 + 16 * jb + r;
-      if (j < N) {
+      if (SPLIT && j < N) {
+        const int64_t heads = (int64_t)gridDim.x / ((int64_t)n_units * a.nsplit);
+        float* pp = a.part + (((int64_t)split * heads + bhk) * N + j) * 2 * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int d0 = 16 * db + 4 * g;
+          *reinterpret_cast<f32x4*>(pp + d0) = tau * accK[jb][db];
+          *reinterpret_cast<f32x4*>(pp + D + d0) = accV[jb][db];
+        }
+      }
+      if (!SPLIT && j < N) {
         const int64_t ro = kv_off + (int64_t)j * D;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
@@ -301,7 +326,25 @@ hipError_t launch_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DIRECT>
+hipError_t launch_split_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
+  constexpr int kBCw = NW * 16 * NJ;
+  const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
+  const int total = n_col_tiles * p.B * p.Hkv * a.nsplit;
+  hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, false, true>),
+                     dim3(total), dim3(NW * 64), 0, s, a, p.Hkv, p.Hq / p.Hkv, p.N, p.tau,
+                     n_col_tiles, total);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// The shipped variants of launch_pass2 below (bf16, no mask, d = 64 with tau a power of
+// two, or d = 128), in split form; split_plan admits no other problem.
+hipError_t launch_pass2_split(const Problem& p, const Pass2Args& a, hipStream_t s) {
+  if (p.d == 64) return launch_split_t<__bf16, 64, 8, 2, 64, 4, kTauPow2, true>(p, a, s);
+  return launch_split_t<__bf16, 128, 8, 1, 64, false, kTauValu, true>(p, a, s);
+}
 
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s) {
   if (p.bf16) {

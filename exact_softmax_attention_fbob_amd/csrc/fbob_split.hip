@@ -1,0 +1,168 @@
+// fbob_split.hip - BoB on problems too small to fill the GPU: split sweeps.
+//
+// A Pass 1 work-group owns 128 query rows and a Pass 2 work-group 256 (d = 64) or
+// 128 (d = 128) keys, and one such work-group runs per CU.  When a problem has
+// fewer tiles than about two rounds of the 256 CUs, whole rounds are left partly
+// idle (B=1 H=12 N=4096 d=64: 384 Pass 1 work-groups, 1.5 rounds; 192 Pass 2
+// work-groups, a quarter of the CUs idle).  The split form divides each row tile's
+// key sweep (Pass 1) or each column tile's row sweep (Pass 2) into s parts run by
+// consecutive work-groups, each writing fp32 partial sums to a workspace, and a
+// short reduction adds the parts in a fixed order (deterministic) and applies what
+// the single-sweep epilogue does:
+//   Pass 1 (FlashBoB notes, "关键设计" 1, the affine correction, through R = X + D B):
+//     dQ~ = tau (Omega - alpha X - E' B),  ddO~ = ddO~' - alpha o,  E = E' - alpha D;
+//   Pass 2: dK~ = sum of tau dK~ parts,  dV~ = sum of dV~ parts.
+// Every output is still written exactly once, with no atomics.
+#include "fbob_device.hpp"
+#include "fbob_launch.hpp"
+
+namespace fbob {
+namespace {
+
+constexpr int kCUs = 256;  // MI355X; only the split heuristic depends on it
+
+// Rows of both reductions: one thread per 4 consecutive d values of one row.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_pass1_kernel(Pass1Args a, int64_t rows, int nsplit,
+                                                           float tau) {
+  constexpr int kChunks = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / kChunks;  // flat (b, h, i)
+  if (row >= rows) return;
+  const int d0 = 4 * (int)(idx % kChunks);
+  f32x4 B = splat4(0.f), X = B, W = B, O = B;
+  float al = 0.f, ed = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t prow = (int64_t)s * rows + row;
+    const float* pa = a.part_acc + prow * 4 * D;
+    B += *reinterpret_cast<const f32x4*>(pa + d0);
+    X += *reinterpret_cast<const f32x4*>(pa + D + d0);
+    W += *reinterpret_cast<const f32x4*>(pa + 2 * D + d0);
+    O += *reinterpret_cast<const f32x4*>(pa + 3 * D + d0);
+    al += a.part_rs[2 * prow];
+    ed += a.part_rs[2 * prow + 1];
+  }
+  const int64_t ro = row * D + d0;
+  const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro);
+  *reinterpret_cast<f32x4*>(a.ddOt + ro) = O - al * o;
+  *reinterpret_cast<f32x4*>(a.dQt + ro) = tau * (W - al * X - ed * B);
+  if (d0 == 0) {
+    a.alpha[row] = al;
+    a.E[row] = ed - al * a.D[row];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void reduce_pass2_kernel(Pass2Args a, int64_t rows, int nsplit) {
+  constexpr int kChunks = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / kChunks;  // flat (b, key/value head, j)
+  if (row >= rows) return;
+  const int d0 = 4 * (int)(idx % kChunks);
+  f32x4 k = splat4(0.f), v = k;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* pp = a.part + ((int64_t)s * rows + row) * 2 * D;
+    k += *reinterpret_cast<const f32x4*>(pp + d0);
+    v += *reinterpret_cast<const f32x4*>(pp + D + d0);
+  }
+  *reinterpret_cast<f32x4*>(a.dKt + row * D + d0) = k;
+  *reinterpret_cast<f32x4*>(a.dVt + row * D + d0) = v;
+}
+
+// Parts s in {1, 2, 4, 8} for `units` work-groups whose full sweep takes `sweep_us`
+// and has `stages` stages (at least two per part), with `part_bytes` of partial sums
+// per part.  Estimated time: the rounds of work-groups over the CUs, each 1/s of a
+// sweep, plus writing the partial sums and reading them back in the reduction
+// (~5 TB/s each way) and the reduction's launch; a split is taken only if the
+// estimate is at least 5 % below the unsplit one.  (Calibrated on B=1 H=12 N=4096
+// d=64: Pass 1 290 us unsplit, 242 + 21 us in two parts; Pass 2 198 us unsplit,
+// 186 + 20 us in four.)
+int choose_parts(int64_t units, int64_t stages, double sweep_us, double part_bytes) {
+  auto est = [&](int s) {
+    const double rounds = (double)((units * s + kCUs - 1) / kCUs);
+    const double extra = s > 1 ? 2.0 * s * part_bytes / 5.0e6 + 5.0 : 0.0;
+    return rounds * sweep_us / s + extra;
+  };
+  int best = 1;
+  for (int s = 2; s <= 8; s *= 2) {
+    if (stages < 2 * s) break;
+    if (est(s) < est(best)) best = s;
+  }
+  return est(best) <= 0.95 * est(1) ? best : 1;
+}
+
+}  // namespace
+
+SplitPlan split_plan(const Problem& p) {
+  SplitPlan plan;
+  // The split forms exist for the shipped bf16 variants without a mask.
+  if (!p.bf16 || p.causal || (p.d == 64 && !tau_is_pow2(p.tau))) return plan;
+  const int64_t heads_q = (int64_t)p.B * p.Hq, heads_kv = (int64_t)p.B * p.Hkv;
+  const int64_t stages = (p.N + 63) / 64;  // 64-key / 64-row stages in both passes
+  const int64_t units1 = (p.N + 127) / 128 * heads_q;
+  const int col_tile = p.d == 64 ? 256 : 128;
+  const int64_t units2 = (p.N + col_tile - 1) / col_tile * heads_kv;
+  const int64_t steps2 = stages * (p.Hq / p.Hkv);  // row steps of a column tile
+  // Measured sweep times of one work-group per key (Pass 1) or row step of 64 rows
+  // (Pass 2): ~35 and ~74 ns per key, ~3.1 and ~3.7 us per row step at d = 64 / 128.
+  const double sweep1 = (p.d == 64 ? 0.035 : 0.074) * p.N;
+  const double sweep2 = (p.d == 64 ? 3.1 : 3.7) * steps2;
+  const double part1 = (double)heads_q * p.N * (4 * p.d + 2) * 4;  // bytes of one part
+  const double part2 = (double)heads_kv * p.N * 2 * p.d * 4;
+  plan.s1 = choose_parts(units1, stages, sweep1, part1);
+  plan.s2 = choose_parts(units2, steps2, sweep2, part2);
+  if (plan.s1 > 1) {
+    plan.split_keys = (int)((stages + plan.s1 - 1) / plan.s1 * 64);
+    plan.bytes1 = (int64_t)plan.s1 * heads_q * p.N * (4 * p.d + 2) * 4;
+  }
+  if (plan.s2 > 1) {
+    plan.split_steps = (int)((steps2 + plan.s2 - 1) / plan.s2);
+    plan.bytes2 = (int64_t)plan.s2 * heads_kv * p.N * 2 * p.d * 4;
+  }
+  return plan;
+}
+
+hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass2Args& a2_in,
+                            const SplitPlan& plan, void* workspace, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  if (plan.s1 > 1) {
+    Pass1Args a1 = a1_in;
+    const int64_t rows = (int64_t)p.B * p.Hq * p.N;
+    a1.part_acc = reinterpret_cast<float*>(ws);
+    a1.part_rs = a1.part_acc + (int64_t)plan.s1 * rows * 4 * p.d;
+    a1.nsplit = plan.s1;
+    a1.split_keys = plan.split_keys;
+    hipError_t e = launch_pass1_split(p, a1, s);
+    if (e != hipSuccess) return e;
+    const int64_t threads = rows * (p.d / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (p.d == 64)
+      hipLaunchKernelGGL(reduce_pass1_kernel<64>, grid, dim3(256), 0, s, a1, rows, plan.s1, p.tau);
+    else
+      hipLaunchKernelGGL(reduce_pass1_kernel<128>, grid, dim3(256), 0, s, a1, rows, plan.s1, p.tau);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const hipError_t e = launch_pass1(p, a1_in, s);
+    if (e != hipSuccess) return e;
+  }
+  if (plan.s2 > 1) {
+    Pass2Args a2 = a2_in;
+    const int64_t rows = (int64_t)p.B * p.Hkv * p.N;
+    a2.part = reinterpret_cast<float*>(ws);  // Pass 1's partials are consumed by now
+    a2.nsplit = plan.s2;
+    a2.split_steps = plan.split_steps;
+    hipError_t e = launch_pass2_split(p, a2, s);
+    if (e != hipSuccess) return e;
+    const int64_t threads = rows * (p.d / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (p.d == 64)
+      hipLaunchKernelGGL(reduce_pass2_kernel<64>, grid, dim3(256), 0, s, a2, rows, plan.s2);
+    else
+      hipLaunchKernelGGL(reduce_pass2_kernel<128>, grid, dim3(256), 0, s, a2, rows, plan.s2);
+    return hipGetLastError();
+  }
+  return launch_pass2(p, a2_in, s);
+}
+
+}  // namespace fbob

@@ -15,7 +15,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  * All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing and keeps no state between calls (fbob_bob_ws takes its
+ *    scratch memory from the caller as well).
  *  * Shapes: per-query-head tensors are [B, Hq, N, d] and per-key/value-head
  *    tensors are [B, Hkv, N, d], contiguous, d fastest.  Row vectors (L, D,
  *    alpha, E) are [B, Hq, N].  Hq must be a multiple of Hkv (grouped-query
@@ -149,6 +150,43 @@ int fbob_bob_pass2(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
                    const void* UQ, const void* UK, const void* UV,
                    const float* L, const float* D, const float* alpha, const float* E,
                    float* dKt, float* dVt, void* stream);
+
+/*
+ * Device workspace, in bytes, that fbob_bob_ws can use for this problem (0 when the
+ * problem fills the GPU without splitting: then fbob_bob_ws is fbob_bob).  Same size
+ * arguments as fbob_bob; writes the size to *bytes.  FBOB_ERR_INVALID_ARG if bytes is
+ * NULL; size errors as fbob_bob.  No HIP call.
+ */
+int fbob_bob_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                            float tau, int causal, int64_t* bytes);
+
+/*
+ * fbob_bob with a caller-owned device workspace for problems too small to fill the
+ * GPU (FlashBoB notes, "关键设计" 2: the same two passes).  A Pass 1 work-group owns
+ * 128 query rows and a Pass 2 work-group 256 keys (d = 64) or 128 (d = 128); when a
+ * problem has too few tiles to keep the 256 CUs busy (e.g. B=1 H=12 N=4096 d=64),
+ * each row tile's key sweep, or each column tile's row sweep, is split over 2-8
+ * work-groups that write fp32 partial sums to the workspace, and a reduction kernel
+ * adds them in a fixed order (results are deterministic; they differ from
+ * fbob_bob's only by the order of the fp32 additions) and writes every output once.
+ * Splitting applies to bf16 inputs without a causal mask, d = 64 with tau a power of
+ * two or d = 128.
+ *   workspace       DEVICE pointer, 16-byte aligned, owned by the caller, at least
+ *                   fbob_bob_workspace_size() bytes; NULL (or fewer bytes) runs the
+ *                   unsplit schedule, i.e. exactly fbob_bob.  Its contents on entry
+ *                   are ignored and on return are undefined; it must not overlap any
+ *                   other argument (FBOB_ERR_ALIAS).  Calls sharing one workspace
+ *                   must be ordered (same stream), or they race.
+ * Other arguments, outputs and errors as fbob_bob.
+ */
+int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                float tau, int causal,
+                const void* Q, const void* K, const void* V, const void* dO,
+                const void* UQ, const void* UK, const void* UV,
+                const float* O, const float* L, const float* D,
+                float* dQt, float* dKt, float* dVt, float* ddOt,
+                float* alpha, float* E, void* workspace, int64_t workspace_bytes,
+                void* stream);
 
 /* Static string naming a status code ("unknown status" for other values). */
 const char* fbob_strerror(int status);

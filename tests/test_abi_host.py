@@ -36,7 +36,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["fbob_forward", "fbob_backward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
-         "fbob_strerror", "fbob_version"])
+         "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_strerror", "fbob_version"])
     assert sorted(_lib.PROTOTYPES) == declared_functions()
 
 
@@ -179,3 +179,54 @@ def test_forward_without_do_needs_both_null(lib):
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load_library(str(tmp_path / "libfbob.so"))
+
+
+def ws_size(lib, dtype=1, B=1, Hq=12, Hkv=12, N=4096, d=64, tau=0.125, causal=0):
+    out = ctypes.c_int64(-1)
+    st = lib.fbob_bob_workspace_size(dtype, B, Hq, Hkv, N, d, ctypes.c_float(tau), causal,
+                                     ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_follows_the_split_plan(lib):
+    """B=1 H=12 N=4096 d=64: 384 Pass 1 row tiles (1.5 rounds of 256 CUs) split in two
+    key parts, 192 Pass 2 column tiles split in four row parts; the workspace holds
+    the larger of the two partial sets.  Problems that fill the GPU, causal ones, fp32
+    and a tau that is not a power of two at d = 64 need none."""
+    heads, N, d = 12, 4096, 64
+    p1 = 2 * heads * N * (4 * d + 2) * 4
+    p2 = 4 * heads * N * 2 * d * 4
+    assert ws_size(lib) == (OK, max(p1, p2))
+    assert ws_size(lib, N=16384) == (OK, 0)            # 1536 and 768 tiles: whole rounds
+    assert ws_size(lib, causal=1) == (OK, 0)
+    assert ws_size(lib, dtype=0) == (OK, 0)
+    assert ws_size(lib, tau=0.1) == (OK, 0)
+    # d = 128, grouped heads: Pass 2 splits the (head, row) steps of each K/V tile
+    st, b = ws_size(lib, Hq=8, Hkv=2, N=8192, d=128)
+    assert st == OK and b > 0
+    assert ws_size(lib, N=0) == (OK, 0)
+    assert ws_size(lib, d=96)[0] == UNSUPPORTED
+    assert lib.fbob_bob_workspace_size(1, 1, 1, 1, 64, 64, ctypes.c_float(0.125), 0,
+                                       None) == INVALID
+
+
+def call_bob_ws(lib, workspace, nbytes, N=4096, Hq=12, ptrs=None):
+    p = ptrs or [FakeBuffers(16)[k] for k in range(16)]
+    return lib.fbob_bob_ws(1, 1, Hq, Hq, N, 64, ctypes.c_float(0.125), 0, *p[:16],
+                           workspace, nbytes, ctypes.c_void_p(0))
+
+
+def test_bob_ws_validates_the_workspace(lib):
+    fb = FakeBuffers(17)
+    ptrs = [fb[m] for m in range(16)]
+    need = ws_size(lib)[1]
+    assert call_bob_ws(lib, fb[16], -1, ptrs=ptrs) == INVALID
+    # a workspace inside an output is an alias (checked only when it would be used)
+    inside = ctypes.c_void_p(fb.addrs[10] + 1024)
+    assert call_bob_ws(lib, inside, need, ptrs=ptrs) == ALIAS
+    # a misaligned workspace
+    assert call_bob_ws(lib, ctypes.c_void_p(fb.addrs[16] + 8), need, ptrs=ptrs) == ALIGN
+    # size errors come first; the empty problem launches nothing
+    assert lib.fbob_bob_ws(1, 1, 2, 2, 64, 96, ctypes.c_float(0.125), 0, *ptrs,
+                           fb[16], need, ctypes.c_void_p(0)) == UNSUPPORTED
+    assert call_bob_ws(lib, fb[16], need, N=0, ptrs=ptrs) == OK
