@@ -28,7 +28,7 @@ import os
 
 from ._lib import FbobError, load_library, STATUS  # noqa: F401
 
-__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "bob_ws",
+__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "bob_ws", "bob_noalloc",
            "bob_workspace_size", "load_library", "FbobError", "library_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -259,4 +259,35 @@ def bob_ws(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, workspace=N
           _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
           _p(out["dQt"]), _p(out["dKt"]), _p(out["dVt"]), _p(out["ddOt"]),
           _p(out["alpha"]), _p(out["E"]), _p(workspace), nbytes, _stream(dev))
+    return out
+
+
+def bob_noalloc(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, out=None):
+    """BoB through the C ABI ``fbob_bob_noalloc``: the split schedule of ``bob_ws``
+    with the library's static per-device scratch instead of a workspace.  ``out``
+    (optional) is a dict of preallocated outputs as returned by ``bob``, so that the
+    call itself allocates nothing; otherwise torch allocates them here."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
+    dev = Q.device
+    _row_state(O, L, D, B, Hq, N, d, dev)
+    if out is None:
+        out = dict(dQt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+                   dKt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+                   dVt=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+                   ddOt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+                   alpha=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+                   E=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    shapes = dict(dQt=(B, Hq, N, d), dKt=(B, Hkv, N, d), dVt=(B, Hkv, N, d),
+                  ddOt=(B, Hq, N, d), alpha=(B, Hq, N), E=(B, Hq, N))
+    for k, shp in shapes.items():
+        t = out[k]
+        if (tuple(t.shape) != shp or t.dtype != torch.float32 or t.device != dev
+                or not t.is_contiguous()):
+            raise ValueError(f"out[{k!r}] must be a contiguous float32 {shp} tensor on {dev}")
+    _call(dev, lib.fbob_bob_noalloc, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L),
+          _p(D), _p(out["dQt"]), _p(out["dKt"]), _p(out["dVt"]), _p(out["ddOt"]),
+          _p(out["alpha"]), _p(out["E"]), _stream(dev))
     return out

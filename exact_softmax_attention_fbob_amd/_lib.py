@@ -27,6 +27,7 @@ PROTOTYPES = {
     "fbob_bob_pass2": (_i, _SIZES + [_vp] * 7 + [_vp] * 4 + [_vp] * 2 + [_vp]),
     "fbob_bob_workspace_size": (_i, _SIZES + [ctypes.POINTER(_i64)]),
     "fbob_bob_ws": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp, _i64] + [_vp]),
+    "fbob_bob_noalloc": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp]),
     "fbob_strerror": (ctypes.c_char_p, [_i]),
     "fbob_version": (_i, []),
 }

@@ -4,8 +4,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fbob.h"
 #include "fbob_launch.hpp"
+
+// Static scratch of fbob_bob_noalloc: the split schedule's fp32 partial sums, for
+// callers that cannot allocate.  Each device the library runs on holds its own
+// copy until the process ends.  In host code this name is only a stand-in for the
+// symbol: kernels get the device address looked up once per device
+// (scratch_address below), never the name itself.
+static __device__ __align__(256) char scratch[FBOB_SCRATCH_BYTES];
 
 namespace {
 
@@ -79,6 +88,57 @@ int check_ptrs(const void* const* ins, const int64_t* in_bytes, int n_in, void* 
 
 int finish(hipError_t e) { return e == hipSuccess ? FBOB_OK : FBOB_ERR_HIP; }
 
+// Pointer checks shared by the BoB entry points: the ten inputs, the six outputs
+// and, when it will be used, the workspace of ws_bytes as a seventh output.
+int check_bob_ptrs(const Checked& c, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                   const void* Q, const void* K, const void* V, const void* dO, const void* UQ,
+                   const void* UK, const void* UV, const float* O, const float* L,
+                   const float* D, float* dQt, float* dKt, float* dVt, float* ddOt,
+                   float* alpha, float* E, void* workspace, int64_t ws_bytes) {
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, O, L, D};
+  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, ob, rb, rb};
+  void* outs[] = {dQt, dKt, dVt, ddOt, alpha, E, workspace};
+  const int64_t outb[] = {ob, kob, kob, ob, rb, rb, ws_bytes};
+  return check_ptrs(ins, inb, 10, outs, outb, workspace != nullptr ? 7 : 6);
+}
+
+// Both passes on one stream, split when a workspace is given.
+int run_bob(const Checked& c, const fbob::SplitPlan& plan, fbob::Pass1Args a1,
+            fbob::Pass2Args a2, void* workspace, hipStream_t s) {
+  if (workspace != nullptr) return finish(fbob::launch_bob_split(c.p, a1, a2, plan, workspace, s));
+  if (fbob::launch_pass1(c.p, a1, s) != hipSuccess) return FBOB_ERR_HIP;
+  return finish(fbob::launch_pass2(c.p, a2, s));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, which must be the stream's:
+// looked up with hipGetSymbolAddress on the first call on each device, then cached.
+int scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FBOB_ERR_HIP;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return FBOB_ERR_HIP;
+    if (sdev != dev) return FBOB_ERR_INVALID_ARG;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FBOB_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_address[dev] == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+      return FBOB_ERR_HIP;
+    g_scratch_address[dev] = addr;
+  }
+  *out = g_scratch_address[dev];
+  return FBOB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,6 +153,7 @@ const char* fbob_strerror(int status) {
     case FBOB_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case FBOB_ERR_ALIAS: return "output buffer overlaps another buffer";
     case FBOB_ERR_HIP: return "HIP launch error";
+    case FBOB_ERR_SCRATCH: return "problem needs more than the static scratch (FBOB_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -203,21 +264,38 @@ int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_
   // The split schedule runs only with a workspace that holds its partial sums;
   // otherwise this is fbob_bob.
   const bool split = plan.bytes() > 0 && workspace != nullptr && workspace_bytes >= plan.bytes();
-  const int64_t es = c.p.bf16 ? 2 : 4;
-  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
-  const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
-  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, O, L, D};
-  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, ob, rb, rb};
-  void* outs[] = {dQt, dKt, dVt, ddOt, alpha, E, workspace};
-  const int64_t outb[] = {ob, kob, kob, ob, rb, rb, plan.bytes()};
-  const int st = check_ptrs(ins, inb, 10, outs, outb, split ? 7 : 6);
+  void* ws = split ? workspace : nullptr;
+  const int st = check_bob_ptrs(c, B, Hq, Hkv, N, d, Q, K, V, dO, UQ, UK, UV, O, L, D, dQt,
+                                dKt, dVt, ddOt, alpha, E, ws, plan.bytes());
   if (st != FBOB_OK) return st;
+  return run_bob(c, plan, fbob::Pass1Args{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E},
+                 fbob::Pass2Args{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt}, ws,
+                 static_cast<hipStream_t>(stream));
+}
+
+int fbob_bob_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     float tau, int causal, const void* Q, const void* K, const void* V,
+                     const void* dO, const void* UQ, const void* UK, const void* UV,
+                     const float* O, const float* L, const float* D, float* dQt, float* dKt,
+                     float* dVt, float* ddOt, float* alpha, float* E, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (c.empty) return FBOB_OK;
+  const int st = check_bob_ptrs(c, B, Hq, Hkv, N, d, Q, K, V, dO, UQ, UK, UV, O, L, D, dQt,
+                                dKt, dVt, ddOt, alpha, E, nullptr, 0);
+  if (st != FBOB_OK) return st;
+  const fbob::SplitPlan plan = fbob::split_plan(c.p);
+  if (plan.bytes() > FBOB_SCRATCH_BYTES) return FBOB_ERR_SCRATCH;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  fbob::Pass1Args a1{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E};
-  fbob::Pass2Args a2{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
-  if (split) return finish(fbob::launch_bob_split(c.p, a1, a2, plan, workspace, s));
-  if (fbob::launch_pass1(c.p, a1, s) != hipSuccess) return FBOB_ERR_HIP;
-  return finish(fbob::launch_pass2(c.p, a2, s));
+  void* ws = nullptr;
+  if (plan.bytes() > 0) {
+    // Every partial a split launch reads is written earlier in the same call, so
+    // the scratch needs no clearing.
+    const int sa = scratch_address(s, &ws);
+    if (sa != FBOB_OK) return sa;
+  }
+  return run_bob(c, plan, fbob::Pass1Args{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E},
+                 fbob::Pass2Args{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt}, ws, s);
 }
 
 int fbob_bob(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
@@ -228,21 +306,13 @@ int fbob_bob(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
   Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
   if (c.status != FBOB_OK) return c.status;
   if (c.empty) return FBOB_OK;
-  const int64_t es = c.p.bf16 ? 2 : 4;
-  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
-  const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
-  const void* ins[] = {Q, K, V, dO, UQ, UK, UV, O, L, D};
-  const int64_t inb[] = {qb, kb, kb, qb, qb, kb, kb, ob, rb, rb};
-  void* outs[] = {dQt, dKt, dVt, ddOt, alpha, E};
-  const int64_t outb[] = {ob, kob, kob, ob, rb, rb};
-  const int st = check_ptrs(ins, inb, 10, outs, outb, 6);
+  const int st = check_bob_ptrs(c, B, Hq, Hkv, N, d, Q, K, V, dO, UQ, UK, UV, O, L, D, dQt,
+                                dKt, dVt, ddOt, alpha, E, nullptr, 0);
   if (st != FBOB_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  fbob::Pass1Args a1{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E};
-  hipError_t e = fbob::launch_pass1(c.p, a1, s);
-  if (e != hipSuccess) return FBOB_ERR_HIP;
-  fbob::Pass2Args a2{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
-  return finish(fbob::launch_pass2(c.p, a2, s));
+  return run_bob(c, fbob::SplitPlan{},
+                 fbob::Pass1Args{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E},
+                 fbob::Pass2Args{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt}, nullptr,
+                 static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -42,6 +42,8 @@
  *      FBOB_ERR_ALIGNMENT    a pointer not 16-byte aligned
  *      FBOB_ERR_ALIAS        an output range overlaps an input or another output
  *      FBOB_ERR_HIP          a HIP launch error (hipGetLastError after launch)
+ *      FBOB_ERR_SCRATCH      fbob_bob_noalloc only: the problem's split schedule
+ *                            needs more than FBOB_SCRATCH_BYTES
  */
 #ifndef FBOB_H_
 #define FBOB_H_
@@ -60,8 +62,12 @@ typedef enum {
   FBOB_ERR_UNSUPPORTED = 2,
   FBOB_ERR_ALIGNMENT = 3,
   FBOB_ERR_ALIAS = 4,
-  FBOB_ERR_HIP = 5
+  FBOB_ERR_HIP = 5,
+  FBOB_ERR_SCRATCH = 6
 } fbob_status;
+
+/* Size of the static per-device scratch array used by fbob_bob_noalloc. */
+#define FBOB_SCRATCH_BYTES ((int64_t)128 << 20)
 
 typedef enum { FBOB_DTYPE_F32 = 0, FBOB_DTYPE_BF16 = 1 } fbob_dtype;
 
@@ -187,6 +193,34 @@ int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_
                 float* dQt, float* dKt, float* dVt, float* ddOt,
                 float* alpha, float* E, void* workspace, int64_t workspace_bytes,
                 void* stream);
+
+/*
+ * fbob_bob_ws without a caller-provided workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  When the problem's split
+ * schedule needs a workspace (fbob_bob_workspace_size > 0) its partial sums go to a
+ * static device array of FBOB_SCRATCH_BYTES (128 MiB) that the library holds on each
+ * device it runs on until the process ends; the library allocates nothing and
+ * issues no memset (every partial a call reads is written earlier in that call).
+ *   * FBOB_ERR_SCRATCH, before any HIP call, if the workspace size exceeds
+ *     FBOB_SCRATCH_BYTES (e.g. B=1 H=12 N=4096 d=128 needs ~202 MB); fbob_bob or
+ *     fbob_bob_ws serve such problems.
+ *   * All calls on one device share that device's array: calls that overlap in
+ *     time on one device (on different streams, or from threads without an order
+ *     between them) race and give wrong results.  Calls on one stream are ordered.
+ *   * `stream` must belong to the current device (FBOB_ERR_INVALID_ARG otherwise);
+ *     the array's device address is looked up once per device, on the first call
+ *     there that splits.
+ * Arguments, outputs and the other errors as fbob_bob; the results are those of
+ * fbob_bob_ws with a large enough workspace, bitwise.
+ */
+int fbob_bob_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     float tau, int causal,
+                     const void* Q, const void* K, const void* V, const void* dO,
+                     const void* UQ, const void* UK, const void* UV,
+                     const float* O, const float* L, const float* D,
+                     float* dQt, float* dKt, float* dVt, float* ddOt,
+                     float* alpha, float* E, void* stream);
 
 /* Static string naming a status code ("unknown status" for other values). */
 const char* fbob_strerror(int status);

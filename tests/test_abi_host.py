@@ -17,7 +17,8 @@ from exact_softmax_attention_fbob_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fbob.h")
 
-OK, INVALID, UNSUPPORTED, ALIGN, ALIAS = 0, 1, 2, 3, 4
+OK, INVALID, UNSUPPORTED, ALIGN, ALIAS, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6
+SCRATCH_BYTES = 128 << 20
 
 
 def declared_functions():
@@ -36,7 +37,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["fbob_forward", "fbob_backward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
-         "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_strerror", "fbob_version"])
+         "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_bob_noalloc", "fbob_strerror",
+         "fbob_version"])
     assert sorted(_lib.PROTOTYPES) == declared_functions()
 
 
@@ -44,8 +46,8 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert lib.fbob_version() == 1
-    for st in range(6):
-        assert lib.fbob_strerror(st)
+    for st in range(7):
+        assert lib.fbob_strerror(st) != b"unknown status"
     assert lib.fbob_strerror(99) == b"unknown status"
 
 
@@ -229,3 +231,35 @@ def test_bob_ws_validates_the_workspace(lib):
     assert lib.fbob_bob_ws(1, 1, 2, 2, 64, 96, ctypes.c_float(0.125), 0, *ptrs,
                            fb[16], need, ctypes.c_void_p(0)) == UNSUPPORTED
     assert call_bob_ws(lib, fb[16], need, N=0, ptrs=ptrs) == OK
+
+
+def test_header_states_the_scratch_size():
+    text = open(HEADER).read()
+    assert re.search(r"#define FBOB_SCRATCH_BYTES \(\(int64_t\)128 << 20\)", text)
+    assert "FBOB_ERR_SCRATCH = 6" in text
+
+
+def call_bob_noalloc(lib, B=1, Hq=12, Hkv=12, N=4096, d=64, ptrs=None):
+    p = ptrs or [FakeBuffers(16)[k] for k in range(16)]
+    return lib.fbob_bob_noalloc(1, B, Hq, Hkv, N, d, ctypes.c_float(1 / d ** 0.5), 0, *p[:16],
+                                ctypes.c_void_p(0))
+
+
+def test_bob_noalloc_validates_before_any_hip_call(lib):
+    """Errors that need no GPU: sizes, pointers, and a split schedule larger than the
+    static scratch (B=1 H=12 N=4096 d=128: Pass 1 in two parts of 12 x 4096 rows x
+    (4 x 128 + 2) fp32, ~202 MB > 128 MiB)."""
+    st, need = ws_size(lib, N=4096, d=128, tau=1 / 128 ** 0.5)
+    assert st == OK and need > SCRATCH_BYTES
+    assert call_bob_noalloc(lib, d=128) == SCRATCH
+    # the C2 problem fits (its workspace is 96.75 MiB)
+    assert 0 < ws_size(lib)[1] <= SCRATCH_BYTES
+    assert call_bob_noalloc(lib, d=96) == UNSUPPORTED
+    assert call_bob_noalloc(lib, N=0) == OK
+    fb = FakeBuffers(16)
+    ptrs = [fb[m] for m in range(16)]
+    ptrs[3] = ctypes.c_void_p(0)
+    assert call_bob_noalloc(lib, d=128, ptrs=ptrs) == INVALID      # pointers before scratch
+    ptrs = [fb[m] for m in range(16)]
+    ptrs[10] = ctypes.c_void_p(fb.addrs[0])                         # dQ~ on top of Q
+    assert call_bob_noalloc(lib, d=128, ptrs=ptrs) == ALIAS
