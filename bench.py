@@ -460,6 +460,63 @@ def fill_sweep(args):
         torch.cuda.empty_cache()
 
 
+def causal_ab(args):
+    """Causal against non-causal at equal unmasked work, interleaved on one box: the
+    pages' causal shape B=4 H=12 N=16384 d=64 (4 N (N + 1) / 2 unmasked pairs per head
+    index) against the same shape without the mask at B=2 (2 N^2).  Six rounds, each
+    timing Pass 1 and Pass 2 of both (HIP events, mean of 10 calls after 3); medians
+    over the rounds.  One JSON line."""
+    import json as _json
+    import statistics
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    import workloads
+
+    def prep(w):
+        T = {k: torch.from_numpy(v).cuda().to(torch.bfloat16)
+             for k, v in workloads.make_inputs(w).items()}
+        a7 = tuple(T[k] for k in workloads.TENSORS)
+        O, L, D = fb.forward(*a7[:4], w.tau, w.causal)
+        p1 = fb.bob_pass1(*a7, O, L, D, w.tau, w.causal)
+        return w, a7, O, L, D, p1
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    causal = workloads.WORKLOADS["pages_causal_b4_h12_n16384_d64_bf16"]
+    plain = causal.with_(name="noncausal_b2_h12_n16384_d64_bf16", B=2, causal=False)
+    cases = {"causal_b4": prep(causal), "noncausal_b2": prep(plain)}
+    res = {k: {"pass1": [], "pass2": []} for k in cases}
+    for rnd in range(6):
+        for k, (w, a7, O, L, D, p1) in cases.items():
+            res[k]["pass1"].append(timed(lambda: fb.bob_pass1(*a7, O, L, D, w.tau, w.causal)))
+            res[k]["pass2"].append(timed(
+                lambda: fb.bob_pass2(*a7, L, D, p1["alpha"], p1["E"], w.tau, w.causal)))
+        print(f"[causal-ab] round {rnd} done", file=sys.stderr, flush=True)
+    med = {k: {p: statistics.median(v[p]) for p in v} for k, v in res.items()}
+    n = causal.N
+    flops = {"causal_b4": 38.0 * n * (n + 1) / 2 * causal.d * causal.B * causal.H,
+             "noncausal_b2": 38.0 * n * n * plain.d * plain.B * plain.H}
+    out = {"median_ms": {k: {p: round(v, 4) for p, v in m.items()} for k, m in med.items()},
+           "bob_tflops": {k: round(flops[k] / ((m["pass1"] + m["pass2"]) * 1e-3) / 1e12, 1)
+                          for k, m in med.items()},
+           "causal_time_per_work_over_noncausal": {
+               p: round(med["causal_b4"][p] / med["noncausal_b2"][p]
+                        * flops["noncausal_b2"] / flops["causal_b4"], 4)
+               for p in ("pass1", "pass2")}}
+    out["bob_rate_ratio"] = round(out["bob_tflops"]["causal_b4"] / out["bob_tflops"]["noncausal_b2"], 4)
+    print(_json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -476,6 +533,8 @@ def main():
                     help="sweep N for one long head instead of the headline step")
     ap.add_argument("--fill-sweep", action="store_true",
                     help="time the passes at N=4096 d=64 for 2..24 heads (GPU fill level)")
+    ap.add_argument("--causal-ab", action="store_true",
+                    help="causal B=4 vs non-causal B=2 at H=12 N=16384 d=64, interleaved")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
     ap.add_argument("--max-n-rows", type=int, default=16,
                     help="rows per length checked against the fp64 oracle in the max-N sweep")
@@ -505,6 +564,13 @@ def main():
             sys.exit(3)
         fb.load_library()
         fill_sweep(args)
+        return
+    if args.causal_ab:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(3)
+        fb.load_library()
+        causal_ab(args)
         return
 
     name = args.workload or workloads.HEADLINE
