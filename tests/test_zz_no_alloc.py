@@ -84,3 +84,53 @@ def test_noalloc_without_split_equals_fbob_bob():
     got = fb.bob_noalloc(*args, O, L, D, w.tau, True, out=outputs_like(ref))
     torch.cuda.synchronize()
     assert_same(got, ref, w.name)
+
+
+def test_split_and_noalloc_under_hip_graph_capture():
+    """The callers the allocation-free entry point is for: forward + fbob_bob_ws (with a
+    preallocated workspace) + fbob_bob_noalloc (preallocated outputs) captured in one
+    HIP graph on a problem that splits.  New inputs are copied into the captured
+    buffers before each of three replays, with eager work in between; every replay
+    must equal the eager fbob_bob_ws result on the same inputs bitwise."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    names = ("Q", "K", "V", "dO", "UQ", "UK", "UV")
+    ws_list = [small(f"noalloc_graph_n1000_h2_s{s}", 1, 2, 1000, 64, 80 + s) for s in range(3)]
+    U.say("[noalloc] hip graph capture of the split schedule, 3 replays")
+    inputs = [U.to_device(U.make_inputs(w), w.dtype) for w in ws_list]
+    static = {k: inputs[0][k].clone() for k in names}
+    tau = ws_list[0].tau
+    need = fb.bob_workspace_size(static["Q"], static["K"], tau)
+    assert 0 < need <= 128 << 20
+    work = torch.empty(need, dtype=torch.uint8, device=static["Q"].device)
+
+    def eager(t):
+        O, L, D = fb.forward(t["Q"], t["K"], t["V"], t["dO"], tau)
+        return fb.bob_ws(*(t[k] for k in names), O, L, D, tau, workspace=work)
+
+    first = eager(static)
+    out_na = outputs_like(first)
+
+    def run(t):
+        O, L, D = fb.forward(t["Q"], t["K"], t["V"], t["dO"], tau)
+        a = fb.bob_ws(*(t[k] for k in names), O, L, D, tau, workspace=work)
+        b = fb.bob_noalloc(*(t[k] for k in names), O, L, D, tau, out=out_na)
+        return a, b
+
+    run(static)  # warm-up outside the capture (the scratch address is looked up here)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap_ws, cap_na = run(static)
+    torch.cuda.synchronize()
+    for rep, t in enumerate(inputs):
+        ref = eager(t)
+        ref = {k: v.clone() for k, v in ref.items()}
+        torch.cuda.synchronize()
+        for k in names:
+            static[k].copy_(t[k])
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(cap_ws[k], ref[k]), ("bob_ws", rep, k)
+            assert torch.equal(cap_na[k], ref[k]), ("bob_noalloc", rep, k)
