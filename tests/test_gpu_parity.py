@@ -53,6 +53,10 @@ SMALL = [
     case("n190_h2_bf16_tau0.3_causal", 1, 2, 190, 64, "bf16", 24, causal=True, tau=0.3),
     case("n160_d128_bf16_tau0.25", 1, 1, 160, 128, "bf16", 25, tau=0.25),
     case("n90_f32_tau0.2", 1, 1, 90, 64, "f32", 26, tau=0.2),
+    # grouped heads with d = 128 and a mask, with fp32 inputs, and with B > 1
+    case("gqa_hq4_hkv2_n150_d128_bf16_causal", 1, 4, 150, 128, "bf16", 32, causal=True, Hkv=2),
+    case("gqa_hq4_hkv1_n70_f32", 1, 4, 70, 64, "f32", 33, Hkv=1),
+    case("gqa_b2_hq4_hkv2_n130_bf16_causal", 2, 4, 130, 64, "bf16", 34, causal=True, Hkv=2),
 ]
 
 
@@ -67,6 +71,30 @@ def test_small_cases_full_oracle(w):
     tol = U.TOL[w.dtype]
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{w.name}: over {tol}: {bad}"
+
+
+UNIFORM_CASES = [case("uniform_n240_h2_bf16", 1, 2, 240, 64, "bf16", 35),
+                 case("uniform_n200_h1_bf16_causal", 1, 1, 200, 64, "bf16", 36, causal=True),
+                 case("uniform_n130_d128_bf16", 1, 1, 130, 128, "bf16", 37)]
+
+
+@pytest.mark.parametrize("w", UNIFORM_CASES, ids=[w.name for w in UNIFORM_CASES])
+def test_uniform_rows(w):
+    """Q = 0: every score is 0, so each row's softmax is uniform over its visible keys
+    (all N, or j <= i with the mask) and the running maximum never moves.  L has the
+    closed form ln(number of visible keys), checked directly; every output is checked
+    against the oracle on the same inputs."""
+    U.say(f"[parity] {w.name}: Q = 0")
+    inp = U.make_inputs(w)
+    inp["Q"] = np.zeros_like(inp["Q"])
+    gpu = U.run_gpu(U.to_device(inp, w.dtype), w.tau, w.causal)
+    visible = np.arange(1, w.N + 1) if w.causal else np.full(w.N, w.N)
+    L_closed = np.broadcast_to(np.log(visible.astype(np.float64)), gpu["L"].shape)
+    assert np.abs(gpu["L"] - L_closed).max() <= 1e-5 * np.log(w.N), "L != ln(visible keys)"
+    errs = U.compare_full(gpu, U.oracle_full(inp, w), w)
+    U.say(f"[parity] {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= U.TOL[w.dtype]}
+    assert not bad, f"{w.name}: over {U.TOL[w.dtype]}: {bad}"
 
 
 def test_gpt2_heads_full_oracle():
