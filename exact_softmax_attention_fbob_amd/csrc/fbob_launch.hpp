@@ -45,7 +45,8 @@ struct Pass1Args {
   float *dQt, *ddOt, *alpha, *E;
   // Split key sweep (small grids): part_acc[s][B Hq][N][4][d] holds the four
   // accumulators (B, X, Omega, ddO~') of split s, part_rs[s][B Hq][N][2] its alpha
-  // and E' partial sums; split s covers keys s * split_keys .. + split_keys - 1.
+  // and (where it is summed over keys) E' partial sums; split s covers keys
+  // s * split_keys .. + split_keys - 1.
   float *part_acc = nullptr, *part_rs = nullptr;
   int nsplit = 1, split_keys = 0;
 };

@@ -3,16 +3,20 @@
 // FlashBoB notes, "关键设计" item 2 (first pass) with the affine decomposition of
 // item 1.  For each query row i it streams every key tile j and accumulates
 //   alpha_i  = sum_j P_ij F_ij                       F = tau (U_Q K^T + Q U_K^T)
-//   E'_i     = sum_j P_ij dP~'_ij                    dP~' = F o (dP - D) + G, G = dO U_V^T
 //   B_i      = sum_j P_ij K_j
 //   X_i      = sum_j dS_ij K_j                       dS = P o (dP - D), dP = dO V^T
-//   Omega_i  = sum_j P_ij dP~'_ij K_j + dS_ij U_K,j
+//   Omega_i  = sum_j P_ij dP~'_ij K_j + dS_ij U_K,j  dP~' = F o (dP - D) + G, G = dO U_V^T
 //   ddO~'_i  = sum_j P_ij F_ij V_j + P_ij U_V,j
 // with P = exp(tau Q K^T - L) rebuilt from the stored log-partition L.  The
 // printed correction dQ~ = tau (Omega - alpha R - E B), with R = sum_j P dP K and
-// E = E' - alpha D, is applied through R = X + D B, which gives
-//   dQ~ = tau (Omega - alpha X - E' B),  ddO~ = ddO~' - alpha O,  E = E' - alpha D
-// and dQ~, ddO~, alpha and E are written exactly once per row.
+// E = E' - alpha D, E'_i = sum_j P_ij dP~'_ij, is applied through R = X + D B:
+//   dQ~ = tau (Omega - alpha X - E' B),  ddO~ = ddO~' - alpha O,  E = E' - alpha D.
+// Expanding dP~' gives
+//   E'_i = sum_j P F dP + P G - alpha_i D_i = <dO_i, ddO~'_i> - alpha_i <dO_i, O_i>
+//        = <dO_i, ddO~_i>,
+// so where alpha is an MFMA row sum (d = 64) E' is that dot product of the corrected
+// row, formed once at the end instead of summed over the keys.  dQ~, ddO~, alpha and E
+// are written exactly once per row.
 //
 // Schedule: one work-group = NW waves; each wave owns 16 query rows whose Q,
 // tau Q, tau U_Q and dO operand fragments and the fp32 accumulators stay in
@@ -25,12 +29,12 @@
 // reads, and the outputs are accumulated transposed so that every row scalar is
 // lane-local.  Row scalars enter as MFMA accumulator seeds (the dP tile starts at
 // -D, giving dP - D directly), tau is folded into the resident operands of the F
-// tile, and the row sums alpha and E' are MFMA contractions with a ones operand,
-// which leaves seven VALU operations plus one exp per score element.  At d = 128
-// (twice the accumulators) the register budget of two waves per SIMD is met by
-// keeping the operands unscaled (tau applied to the F tile on the VALU), taking
-// the row sums as lane-local fp32 sums, and keeping one LDS offset per access
-// pattern.
+// tile, and the row sum alpha is an MFMA contraction with a ones operand, which
+// leaves seven VALU operations plus one exp per score element (E' comes from the
+// identity below).  At d = 128 (twice
+// the accumulators) the register budget of two waves per SIMD is met by keeping the
+// operands unscaled (tau applied to the F tile on the VALU), taking alpha and E' as
+// lane-local fp32 sums, and keeping one LDS offset per access pattern.
 #include <type_traits>
 
 #include "fbob_device.hpp"
@@ -44,7 +48,7 @@ namespace {
 // of the MFMAs that use them, with the order pinned by sched_group_barrier; 3 is 2
 // with raised wave priority over the contraction MFMAs, 4 also over the score
 // MFMAs.
-// VSUM: the row sums alpha, E' as lane-local fp32 sums of the unrounded products
+// VSUM: the row sums alpha and E' as lane-local fp32 sums of the unrounded products
 // (the d = 128 and multi-row-block layouts always do this).
 // SPLIT (no mask): the work-group sweeps one part of the keys and writes its raw
 // accumulators and row sums to a.part_acc / a.part_rs; a reduction kernel adds the
@@ -119,15 +123,17 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
       dv[ib] = i < N ? a.D[(int64_t)bh * N + i] : 0.f;
     }
-    // Row sums by MFMA: an operand of ones in rows 0..7 (for alpha) or rows 8..15
-    // (for E') makes C rows 0..7 hold sum_j P F and rows 8..15 sum_j P dP~'.  Lane
-    // (r, g) therefore holds alpha of row r for g < 2 and E' for g >= 2.
+    // The row sum alpha = sum_j P F by MFMA: an operand of ones in rows 0..7 makes C
+    // rows 0..7 hold it, so lane (r, g) holds alpha of row r for g < 2.
     const F onesA = r < 8 ? ones_frag<T>() : zero_frag<T>();
-    const F onesE = r < 8 ? zero_frag<T>() : ones_frag<T>();
-    // At d = 128 the registers of the two ones operands are worth more than the VALU
-    // adds: there the row sums are lane-local fp32 partial sums (keys 4 g + q of row
-    // r), reduced over the four lanes of a row at the end.
+    // At d = 128 the register of the ones operand is worth more than the VALU adds:
+    // there alpha and E' are lane-local fp32 partial sums (keys 4 g + q of row r),
+    // reduced over the four lanes of a row at the end.
     constexpr bool kVsum = D >= 128 || NI >= 2 || VSUM;
+    // With alpha summed from the same bf16-rounded P F that feed ddO~', E' is taken
+    // as <dO_i, ddO~_i> at the end (the rounding of P F cancels in ddO~' - alpha o and
+    // thus in E'); with an fp32 alpha it would not, so E' is summed over the keys.
+    constexpr bool kEdot = !kVsum;
     float asum[NI], esum[NI];
 
     f32x4 accB[NI][kDB], accX[NI][kDB], accW[NI][kDB], accO[NI][kDB];
@@ -280,11 +286,8 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       const auto rx = rd.fresh();
       if constexpr (!kVsum) {
 #pragma unroll
-        for (int ib = 0; ib < NI; ++ib) {
-          accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
-          accAE[ib] = E::mma(onesE, fr.pw[ib], accAE[ib]);
-        }
-        if constexpr (kPipe) FBOB_SGB(kSgMfma, 2 * NI);
+        for (int ib = 0; ib < NI; ++ib) accAE[ib] = E::mma(onesA, fr.pf[ib], accAE[ib]);
+        if constexpr (kPipe) FBOB_SGB(kSgMfma, NI);
       }
       // kPipe: the transposed fragments of column block db + 1 are read while
       // block db's MFMAs run (two register slots; each read is two instructions).
@@ -388,12 +391,15 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     }
 
     // ---- row correction and the single write of each row output ----
+    // E' = E + alpha D equals <dO_i, ddO~_i> exactly (ddO~ = ddO~' - alpha o, and the
+    // sum over keys of P dP~' expands to the same products), so it is formed from the
+    // corrected ddO~ row here instead of being accumulated over the keys.
 #pragma unroll
     for (int ib = 0; ib < NI; ++ib) {
       const int i = iw0 + 16 * ib + r;
       // F carries tau through the scaled resident operands.
       const float al = kVsum ? group_sum(asum[ib]) : __shfl(accAE[ib][0], r);
-      const float edeg = kVsum ? group_sum(esum[ib]) : __shfl(accAE[ib][0], 32 + r);
+      const float esum_row = kEdot ? 0.f : group_sum(esum[ib]);
       if constexpr (SPLIT) {
         if (i < N) {
           const int64_t heads = (int64_t)gridDim.x / ((int64_t)n_units * a.nsplit);
@@ -407,20 +413,35 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
             *reinterpret_cast<f32x4*>(pa + 2 * D + d0) = accW[ib][db];
             *reinterpret_cast<f32x4*>(pa + 3 * D + d0) = accO[ib][db];
           }
-          if (g == 0) {
+          if (g == 0) {  // E' of this part when it is summed over keys (else unused)
             a.part_rs[2 * prow] = al;
-            a.part_rs[2 * prow + 1] = edeg;
+            a.part_rs[2 * prow + 1] = esum_row;
           }
         }
         continue;
       }
+      const int64_t ro = q_off + (int64_t)i * D;
+      float dot = 0.f;  // this lane's part of <dO_i, ddO~_i>
       if (i < N) {
-        const int64_t ro = q_off + (int64_t)i * D;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const int d0 = 16 * db + 4 * g;
           const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro + d0);
-          *reinterpret_cast<f32x4*>(a.ddOt + ro + d0) = accO[ib][db] - al * o;
+          accO[ib][db] -= al * o;  // ddO~
+          if constexpr (kEdot) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              dot = __builtin_fmaf((float)dOh[(int64_t)i * D + d0 + q], accO[ib][db][q], dot);
+          }
+        }
+      }
+      // (the four lanes of row i share the branch above)
+      const float edeg = kEdot ? group_sum(dot) : esum_row;
+      if (i < N) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int d0 = 16 * db + 4 * g;
+          *reinterpret_cast<f32x4*>(a.ddOt + ro + d0) = accO[ib][db];
           *reinterpret_cast<f32x4*>(a.dQt + ro + d0) =
               tau * (accW[ib][db] - al * accX[ib][db] - edeg * accB[ib][db]);
         }

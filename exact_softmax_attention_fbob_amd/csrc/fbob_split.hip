@@ -10,7 +10,9 @@
 // short reduction adds the parts in a fixed order (deterministic) and applies what
 // the single-sweep epilogue does:
 //   Pass 1 (FlashBoB notes, "关键设计" 1, the affine correction, through R = X + D B):
-//     dQ~ = tau (Omega - alpha X - E' B),  ddO~ = ddO~' - alpha o,  E = E' - alpha D;
+//     ddO~ = ddO~' - alpha o,  dQ~ = tau (Omega - alpha X - E' B),  E = E' - alpha D,
+//     with E' = <dO, ddO~> where the split kernel forms alpha by MFMA (d = 64), else
+//     the sum of the parts' E';
 //   Pass 2: dK~ = sum of tau dK~ parts,  dV~ = sum of dV~ parts.
 // Every output is still written exactly once, with no atomics.
 #include "fbob_device.hpp"
@@ -21,17 +23,20 @@ namespace {
 
 constexpr int kCUs = 256;  // MI355X; only the split heuristic depends on it
 
-// Rows of both reductions: one thread per 4 consecutive d values of one row.
-template <int D>
+// Rows of both reductions: one thread per 4 consecutive d values of one row (the
+// D / 4 threads of a row are consecutive lanes of one wave).  EDOT: E' as <dO, ddO~>.
+template <typename T, int D, bool EDOT>
 __global__ __launch_bounds__(256) void reduce_pass1_kernel(Pass1Args a, int64_t rows, int nsplit,
                                                            float tau) {
   constexpr int kChunks = D / 4;
+  static_assert(kChunks <= 64 && (kChunks & (kChunks - 1)) == 0, "a row's threads in one wave");
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = idx / kChunks;  // flat (b, h, i)
+  // Whole rows leave together, so the row reduction below only reads live lanes.
   if (row >= rows) return;
   const int d0 = 4 * (int)(idx % kChunks);
   f32x4 B = splat4(0.f), X = B, W = B, O = B;
-  float al = 0.f, ed = 0.f;
+  float al = 0.f, es = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const int64_t prow = (int64_t)s * rows + row;
     const float* pa = a.part_acc + prow * 4 * D;
@@ -40,11 +45,22 @@ __global__ __launch_bounds__(256) void reduce_pass1_kernel(Pass1Args a, int64_t 
     W += *reinterpret_cast<const f32x4*>(pa + 2 * D + d0);
     O += *reinterpret_cast<const f32x4*>(pa + 3 * D + d0);
     al += a.part_rs[2 * prow];
-    ed += a.part_rs[2 * prow + 1];
+    es += a.part_rs[2 * prow + 1];
   }
   const int64_t ro = row * D + d0;
   const f32x4 o = *reinterpret_cast<const f32x4*>(a.O + ro);
-  *reinterpret_cast<f32x4*>(a.ddOt + ro) = O - al * o;
+  const f32x4 ddo = O - al * o;
+  float ed = es;
+  if constexpr (EDOT) {  // E' = <dO, ddO~> of this row
+    const T* dO = reinterpret_cast<const T*>(a.dO) + ro;
+    float dot = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dot = __builtin_fmaf((float)dO[q], ddo[q], dot);
+#pragma unroll
+    for (int m = kChunks / 2; m >= 1; m /= 2) dot += __shfl_xor(dot, m);
+    ed = dot;
+  }
+  *reinterpret_cast<f32x4*>(a.ddOt + ro) = ddo;
   *reinterpret_cast<f32x4*>(a.dQt + ro) = tau * (W - al * X - ed * B);
   if (d0 == 0) {
     a.alpha[row] = al;
@@ -136,10 +152,14 @@ hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass
     if (e != hipSuccess) return e;
     const int64_t threads = rows * (p.d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
+    // split_plan admits bf16 inputs only; the d = 64 split kernel forms alpha by MFMA
+    // (E' from ddO~), the d = 128 one as lane sums (E' summed over the parts)
     if (p.d == 64)
-      hipLaunchKernelGGL(reduce_pass1_kernel<64>, grid, dim3(256), 0, s, a1, rows, plan.s1, p.tau);
+      hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 64, true>), grid, dim3(256), 0, s, a1,
+                         rows, plan.s1, p.tau);
     else
-      hipLaunchKernelGGL(reduce_pass1_kernel<128>, grid, dim3(256), 0, s, a1, rows, plan.s1, p.tau);
+      hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 128, false>), grid, dim3(256), 0, s, a1,
+                         rows, plan.s1, p.tau);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
