@@ -151,8 +151,9 @@ def _check_invariants(w, inp, gpu):
       values themselves are checked against the oracle elsewhere: stored columns,
       full heads, or class-tiled inputs).
     * At every row E = dO . ddO~ - alpha D (dP~ depends on dO only through dP and
-      G): Pass 1 forms E by a reduction over keys, so this ties it to ddO~, alpha
-      and D where the oracle only samples rows."""
+      G).  At d = 128 Pass 1 forms E by a reduction over keys, so this ties it to
+      ddO~, alpha and D where the oracle only samples rows; at d = 64 Pass 1 takes
+      E' = E + alpha D as dO . ddO~ itself, and this checks that arithmetic."""
     for key in ("dKt", "dVt"):
         x = gpu[key]
         s = np.abs(x.sum(axis=2))
