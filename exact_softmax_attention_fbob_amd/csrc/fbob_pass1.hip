@@ -392,8 +392,8 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
 
     // ---- row correction and the single write of each row output ----
     // E' = E + alpha D equals <dO_i, ddO~_i> exactly (ddO~ = ddO~' - alpha o, and the
-    // sum over keys of P dP~' expands to the same products), so it is formed from the
-    // corrected ddO~ row here instead of being accumulated over the keys.
+    // sum over keys of P dP~' expands to the same products); with kEdot it is formed
+    // from the corrected ddO~ row here, otherwise it is the lane sums' total.
 #pragma unroll
     for (int ib = 0; ib < NI; ++ib) {
       const int i = iw0 + 16 * ib + r;
