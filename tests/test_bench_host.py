@@ -99,3 +99,17 @@ def test_cpu_baseline_on_a_tiny_workload():
     r = bench.cpu_baseline(g, budget_s=30.0, max_heads=3)
     assert r["sample"].startswith("192 rows in 3 of 4 heads"), r["sample"]
     assert r["extrapolated_full_bob_s"] > 0
+
+
+@pytest.mark.parametrize("mode", [["--fill-sweep"], ["--causal-ab"], ["--max-n"],
+                                  ["--workspace", "--workload", "gpt2_heads_h12_n4096_d64_bf16"]])
+def test_measurement_modes_parse_and_need_a_gpu(mode):
+    """Each measurement mode parses its arguments and, without a visible GPU, stops with
+    exit status 3 and a message instead of falling back to anything on the CPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *mode],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 3, r.stderr
+    assert "no GPU visible" in r.stderr
