@@ -45,10 +45,10 @@ struct Pass1Args {
   float *dQt, *ddOt, *alpha, *E;
   // Split key sweep (small grids): part_acc[s][B Hq][N][4][d] holds the four
   // accumulators (B, X, Omega, ddO~') of split s, part_rs[s][B Hq][N][2] its alpha
-  // and (where it is summed over keys) E' partial sums; split s covers keys
-  // s * split_keys .. + split_keys - 1.
+  // and (where it is summed over keys) E' partial sums; split s covers the s-th of
+  // nsplit equal shares of a work-group's key stages.
   float *part_acc = nullptr, *part_rs = nullptr;
-  int nsplit = 1, split_keys = 0;
+  int nsplit = 1;
 };
 
 struct Pass2Args {
@@ -56,9 +56,9 @@ struct Pass2Args {
   const float *L, *D, *alpha, *E;
   float *dKt, *dVt;
   // Split row sweep (small grids): part[s][B Hkv][N][2][d] holds tau dK~ and dV~ of
-  // split s, which covers row steps s * split_steps .. + split_steps - 1.
+  // split s, which covers the s-th of nsplit equal shares of a work-group's row steps.
   float* part = nullptr;
-  int nsplit = 1, split_steps = 0;
+  int nsplit = 1;
 };
 
 // How a BoB call spreads small problems over the GPU: each Pass 1 row tile's key
@@ -66,7 +66,6 @@ struct Pass2Args {
 // split), and the device workspace the partial sums need.
 struct SplitPlan {
   int s1 = 1, s2 = 1;
-  int split_keys = 0, split_steps = 0;
   int64_t bytes1 = 0, bytes2 = 0;  // Pass 1 / Pass 2 partials (the two reuse one buffer)
   int64_t bytes() const { return bytes1 > bytes2 ? bytes1 : bytes2; }
 };

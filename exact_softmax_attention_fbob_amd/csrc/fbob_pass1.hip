@@ -50,9 +50,11 @@ namespace {
 // MFMAs.
 // VSUM: the row sums alpha and E' as lane-local fp32 sums of the unrounded products
 // (the d = 128 and multi-row-block layouts always do this).
-// SPLIT (no mask): the work-group sweeps one part of the keys and writes its raw
+// SPLIT: the work-group sweeps one part of its key stages and writes its raw
 // accumulators and row sums to a.part_acc / a.part_rs; a reduction kernel adds the
-// parts and applies the correction.
+// parts and applies the correction.  With the causal pairing the two row tiles' key
+// stages form one sequence, cut into equal parts (a part may end in the first tile and
+// start the second).
 template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT, bool CAUSAL,
           bool VSUM = false, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int group, int N,
@@ -82,7 +84,6 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
   // does not fit the register budget: one tile per work-group, the longest
   // dispatched first.
   constexpr bool kFold = CAUSAL && D < 128;
-  static_assert(!(SPLIT && CAUSAL), "the split sweep is for unmasked problems");
   const int n_units = kFold ? (n_row_tiles + 1) / 2 : n_row_tiles;
   // SPLIT: the parts of one row tile are consecutive work-groups (one XCD).
   const int split = SPLIT ? logical % a.nsplit : 0;
@@ -100,7 +101,23 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
                                 reinterpret_cast<const T*>(a.UK) + kv_off,
                                 reinterpret_cast<const T*>(a.UV) + kv_off};
 
-  auto run_tile = [&](const int rt) {
+  // Key stages of row tile rt (causal: up to its last row) and, under SPLIT, this
+  // part's share [part_lo, part_hi) of the work-group's stages, counted over its tiles
+  // in the order they run.
+  auto key_end = [&](int rt) { return CAUSAL ? min(N, rt * kBR + kBR) : N; };
+  auto stages_of = [&](int rt) { return (key_end(rt) + kBC - 1) / kBC; };
+  const int rt_first = CAUSAL ? n_row_tiles - 1 - unit : unit;
+  const bool two_tiles = kFold && unit != n_row_tiles - 1 - unit;
+  int stages0 = 0, part_lo = 0, part_hi = 0;
+  if constexpr (SPLIT) {
+    stages0 = stages_of(rt_first);
+    const int all = stages0 + (two_tiles ? stages_of(unit) : 0);
+    const int per = (all + a.nsplit - 1) / a.nsplit;
+    part_lo = min(all, split * per);
+    part_hi = min(all, part_lo + per);
+  }
+
+  auto run_tile = [&](const int rt, const int tile) {
     // ---- resident row operands (B operand of the transposed score tiles) ----
     const int iw0 = rt * kBR + w * kRW;
     // tqf / tuqf hold tau Q / tau U_Q, or Q / U_Q unscaled under kTauValu; qf (Q for
@@ -155,9 +172,12 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     // At d = 128 the lane keeps one LDS offset per access pattern (XOR form).
     const LdsLane<T, D, (D >= 128 || NI >= 2)> rd(r, g);
 
-    const int jbeg = SPLIT ? split * a.split_keys : 0;  // a multiple of kBC
-    int jend = SPLIT ? min(N, jbeg + a.split_keys) : N;
-    if (CAUSAL) jend = min(N, rt * kBR + kBR);
+    int jbeg = 0, jend = key_end(rt);  // jbeg a multiple of kBC
+    if constexpr (SPLIT) {
+      const int base = tile == 0 ? 0 : stages0, full = stages_of(rt);
+      jbeg = min(full, max(0, part_lo - base)) * kBC;
+      jend = min(jend, min(full, max(0, part_hi - base)) * kBC);
+    }
     const int ntc = max(jend - jbeg + kBC - 1, 0) / kBC;
 
     // Operand fragments of one 32-key tile for the contractions over keys.
@@ -355,11 +375,11 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       else st.store(buf);
     };
     stage_init();
-    stage_load(lds[0], jbeg);  // rows are clamped to N - 1 (an empty part computes nothing)
+    stage_load(lds[0], jbeg);  // rows are clamped to N - 1 (an empty range computes nothing)
     stage_commit(lds[0]);
     __syncthreads();
 
-    auto active_tile = [&](int t) { return !CAUSAL || t * kBC <= iw0 + kRW - 1; };
+    auto active_tile = [&](int j0) { return !CAUSAL || j0 <= iw0 + kRW - 1; };
     // Both 32-key halves of a stage (BC = 64) or the single one (BC = 32).
     auto compute_stage = [&](const char* cur, int j0) {
 #pragma unroll
@@ -380,7 +400,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
       const int j0 = jbeg + t * kBC;
       const bool more = t + 1 < ntc;
       if (more) stage_load(nxt, j0 + kBC);
-      if (active_tile(t)) compute_stage(cur, j0);
+      if (active_tile(j0)) compute_stage(cur, j0);
       if (more) stage_commit(nxt);
       __syncthreads();
     };
@@ -453,11 +473,11 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
     }
   };
   if constexpr (kFold) {
-    const int n_tiles_here = unit != n_row_tiles - 1 - unit ? 2 : 1;
 #pragma unroll 1
-    for (int tile = 0; tile < n_tiles_here; ++tile) run_tile(tile == 0 ? n_row_tiles - 1 - unit : unit);
+    for (int tile = 0; tile < (two_tiles ? 2 : 1); ++tile)
+      run_tile(tile == 0 ? rt_first : unit, tile);
   } else {
-    run_tile(CAUSAL ? n_row_tiles - 1 - unit : unit);
+    run_tile(rt_first, 0);
   }
 }
 
@@ -483,7 +503,16 @@ template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIR
 hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
-  const int total = n_row_tiles * p.B * p.Hq * a.nsplit;
+  const int n_units = p.causal && D < 128 ? (n_row_tiles + 1) / 2 : n_row_tiles;
+  const int total = n_units * p.B * p.Hq * a.nsplit;
+  if constexpr (D >= 128) {
+    if (p.causal) return hipErrorInvalidValue;  // split_plan masks only at d = 64
+  } else if (p.causal) {
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true, false, true>),
+                       dim3(total), dim3(NW * 64), 0, s, a, p.Hq, p.Hq / p.Hkv, p.N, p.tau,
+                       n_row_tiles, total);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false, false, true>),
                      dim3(total), dim3(NW * 64), 0, s, a, p.Hq, p.Hq / p.Hkv, p.N, p.tau,
                      n_row_tiles, total);
@@ -492,8 +521,9 @@ hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
 
 }  // namespace
 
-// The shipped variants of launch_pass1 below (bf16, no mask, d = 64 with tau a power of
-// two, or d = 128), in split form; split_plan admits no other problem.
+// The shipped bf16 variants of launch_pass1 below (d = 64 with tau a power of two, with
+// or without the causal mask; d = 128 without it), in split form; split_plan admits no
+// other problem.
 hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.d == 64) return launch_split_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
   return launch_split_t<__bf16, 128, 8, 1, true, kTauValu, 32, true>(p, a, s);

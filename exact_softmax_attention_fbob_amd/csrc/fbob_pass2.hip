@@ -39,13 +39,14 @@ namespace {
 // SCHED: 0 leaves instruction order to the compiler, 1 fences the phases and
 // column blocks; 3 raises the wave priority over the contraction MFMAs, 4 also over
 // the score MFMAs (no fences otherwise).
-// SPLIT (no mask): the work-group sweeps one part of the row steps and writes tau dK~
-// and dV~ of that part to a.part; a reduction kernel adds the parts.
+// SPLIT: the work-group sweeps one part of its row steps and writes tau dK~ and dV~
+// of that part to a.part; a reduction kernel adds the parts.  With the causal pairing
+// the two tiles' row steps form one sequence, cut into equal parts (a part may end in
+// the first tile and start the second), so all parts stay equally long.
 template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DIRECT, bool CAUSAL,
           bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, int group, int N,
                                                         float tau, int n_col_tiles, int total) {
-  static_assert(!(SPLIT && CAUSAL), "the split sweep is for unmasked problems");
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr bool FENCE = SCHED == 1;
@@ -83,6 +84,20 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
   const T* UVh = reinterpret_cast<const T*>(a.UV) + kv_off;
 
   const int n_tiles_here = kFold && unit != n_col_tiles - 1 - unit ? 2 : 1;
+  // Row steps (query head of the group, 64-row chunk) of column tile ct; causal rows
+  // start at the chunk holding the tile's first key.
+  auto first_row = [&](int ct) { return CAUSAL ? (ct * kBCw / BRS) * BRS : 0; };
+  auto steps_of = [&](int ct) { return (N - first_row(ct) + BRS - 1) / BRS * group; };
+  // SPLIT: this part's share [part_lo, part_hi) of the work-group's steps, counted
+  // over its tiles in order.
+  int steps0 = 0, part_lo = 0, part_hi = 0;
+  if constexpr (SPLIT) {
+    steps0 = steps_of(unit);
+    const int all_steps = steps0 + (n_tiles_here == 2 ? steps_of(n_col_tiles - 1 - unit) : 0);
+    const int per_part = (all_steps + a.nsplit - 1) / a.nsplit;
+    part_lo = min(all_steps, split * per_part);
+    part_hi = min(all_steps, part_lo + per_part);
+  }
 #pragma unroll 1
   for (int tile = 0; tile < n_tiles_here; ++tile) {
     const int ct = tile == 0 ? unit : n_col_tiles - 1 - unit;
@@ -119,9 +134,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
     const float inv_tau = TM == kTauValu ? 1.f / tau : 1.f;
     const LdsLane<T, D> rd(r, g);
 
-    // Row steps: (query head of the group, row chunk); causal rows start at the
-    // work-group's first key.
-    const int i_begin = CAUSAL ? (ct * kBCw / BRS) * BRS : 0;
+    const int i_begin = first_row(ct);
     const int nrc = (N - i_begin + BRS - 1) / BRS;
     const int nsteps = nrc * group;
 
@@ -139,10 +152,18 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
     // Row scalars: thread tid < BRS stages row tid of the chunk.
     const int64_t s0 = ((int64_t)b * Hq + (int64_t)hk * group) * N;
     f32x4 scal = splat4(0.f);
-    // Issue the loads of step `step` (tiles go straight into `buf` when DIRECT).
-    auto load_step = [&](int step, char* buf) {
-      const int hq = step / nrc;
-      const int i0 = i_begin + (step % nrc) * BRS;
+    // Steps run in order: the next one to load is query head ld_hq, row chunk ld_rc
+    // (advanced by one chunk per load rather than divided out of the step index).
+    int ld_hq = 0, ld_rc = 0, nxt_i0 = 0;
+    // Issue the loads of the next step (tiles go straight into `buf` when DIRECT).
+    auto load_step = [&](char* buf) {
+      const int hq = ld_hq;
+      const int i0 = i_begin + ld_rc * BRS;
+      nxt_i0 = i0;
+      if (++ld_rc == nrc) {
+        ld_rc = 0;
+        ++ld_hq;
+      }
       if constexpr (DIRECT) st.load(buf, i0, N, hq * q_head);
       else st.load(i0, N, hq * q_head);
       // The raw values stay in registers until store_step: deriving the seeds here
@@ -248,22 +269,30 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       if constexpr (kPrioOut) FBOB_PRIO_LOW();
     };
 
-    // This work-group's row steps (all of them unless SPLIT).
-    const int step_lo = SPLIT ? min(nsteps, split * a.split_steps) : 0;
-    const int step_hi = SPLIT ? min(nsteps, step_lo + a.split_steps) : nsteps;
-    // An empty part (possible when the steps do not divide evenly) stages nothing:
-    // step nsteps would address the query head after the group.  Uniform per
-    // work-group, so the barriers below stay uniform too.
+    // This work-group's row steps of the tile (all of them unless SPLIT).
+    int step_lo = 0, step_hi = nsteps;
+    if constexpr (SPLIT) {
+      const int base = tile == 0 ? 0 : steps0;
+      step_lo = min(nsteps, max(0, part_lo - base));
+      step_hi = min(nsteps, max(0, part_hi - base));
+    }
+    // An empty range (a part that does not reach this tile, or the empty last part
+    // when the steps do not divide evenly) stages nothing, and its part of the sums
+    // is written as zeros: step nsteps would address the query head after the group.
+    // Uniform per work-group, so the barriers below stay uniform too.
     if (step_lo < step_hi) {
-    load_step(step_lo, lds[0]);
+    ld_hq = step_lo / nrc;
+    ld_rc = step_lo - ld_hq * nrc;
+    load_step(lds[0]);
     if constexpr (DIRECT) wait_all_memory();
     store_step(lds[0]);
     __syncthreads();
 
+    int cur_i0 = nxt_i0;  // first row of the step staged in `cur`
     auto step = [&](int t, char* cur, char* nxt) {
-      const int i0 = i_begin + (t % nrc) * BRS;
+      const int i0 = cur_i0;
       const bool more = t + 1 < step_hi;
-      if (more) load_step(t + 1, nxt);
+      if (more) load_step(nxt);
 #pragma unroll
       for (int sc = 0; sc < BRS / 32; ++sc) {
         const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
@@ -274,6 +303,7 @@ __global__ __launch_bounds__(NW * 64) void pass2_kernel(Pass2Args a, int Hkv, in
       if constexpr (DIRECT) wait_all_memory();
       if (more) store_step(nxt);
       __syncthreads();
+      cur_i0 = nxt_i0;
     };
 #pragma unroll 1
     for (int t = step_lo; t < step_hi; t += 2) {
@@ -330,7 +360,16 @@ template <typename T, int D, int NW, int NJ, int BRS, int SCHED, int TM, bool DI
 hipError_t launch_split_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   constexpr int kBCw = NW * 16 * NJ;
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
-  const int total = n_col_tiles * p.B * p.Hkv * a.nsplit;
+  const int n_units = p.causal && D < 128 ? (n_col_tiles + 1) / 2 : n_col_tiles;
+  const int total = n_units * p.B * p.Hkv * a.nsplit;
+  if constexpr (D >= 128) {
+    if (p.causal) return hipErrorInvalidValue;  // split_plan masks only at d = 64
+  } else if (p.causal) {
+    hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, true, true>),
+                       dim3(total), dim3(NW * 64), 0, s, a, p.Hkv, p.Hq / p.Hkv, p.N, p.tau,
+                       n_col_tiles, total);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, false, true>),
                      dim3(total), dim3(NW * 64), 0, s, a, p.Hkv, p.Hq / p.Hkv, p.N, p.tau,
                      n_col_tiles, total);
@@ -339,8 +378,9 @@ hipError_t launch_split_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
 
 }  // namespace
 
-// The shipped variants of launch_pass2 below (bf16, no mask, d = 64 with tau a power of
-// two, or d = 128), in split form; split_plan admits no other problem.
+// The shipped bf16 variants of launch_pass2 below (d = 64 with tau a power of two, with
+// or without the causal mask; d = 128 without it), in split form; split_plan admits no
+// other problem.
 hipError_t launch_pass2_split(const Problem& p, const Pass2Args& a, hipStream_t s) {
   if (p.d == 64) return launch_split_t<__bf16, 64, 8, 2, 64, 4, kTauPow2, true>(p, a, s);
   return launch_split_t<__bf16, 128, 8, 1, 64, false, kTauValu, true>(p, a, s);

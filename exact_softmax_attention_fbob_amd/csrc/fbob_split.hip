@@ -14,7 +14,11 @@
 //     with E' = <dO, ddO~> where the split kernel forms alpha by MFMA (d = 64), else
 //     the sum of the parts' E';
 //   Pass 2: dK~ = sum of tau dK~ parts,  dV~ = sum of dV~ parts.
-// Every output is still written exactly once, with no atomics.
+// Every output is still written exactly once, with no atomics.  With the causal mask
+// (d = 64) a Pass 2 work-group sweeps two column tiles, p and n - 1 - p, whose row
+// steps together are the same for every pair; the split cuts that joint sweep into
+// equal parts; causal Pass 1 pairs its row tiles n - 1 - p and p, and splits the
+// same way.
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
@@ -111,30 +115,45 @@ int choose_parts(int64_t units, int64_t stages, double sweep_us, double part_byt
 
 SplitPlan split_plan(const Problem& p) {
   SplitPlan plan;
-  // The split forms exist for the shipped bf16 variants without a mask.
-  if (!p.bf16 || p.causal || (p.d == 64 && !tau_is_pow2(p.tau))) return plan;
+  // The split forms exist for the shipped bf16 variants; with the causal mask only at
+  // d = 64, where the tiles of both passes are paired.
+  if (!p.bf16 || (p.d == 64 && !tau_is_pow2(p.tau))) return plan;
+  if (p.causal && p.d != 64) return plan;
   const int64_t heads_q = (int64_t)p.B * p.Hq, heads_kv = (int64_t)p.B * p.Hkv;
+  const int64_t group = p.Hq / p.Hkv;
   const int64_t stages = (p.N + 63) / 64;  // 64-key / 64-row stages in both passes
-  const int64_t units1 = (p.N + 127) / 128 * heads_q;
   const int col_tile = p.d == 64 ? 256 : 128;
-  const int64_t units2 = (p.N + col_tile - 1) / col_tile * heads_kv;
-  const int64_t steps2 = stages * (p.Hq / p.Hkv);  // row steps of a column tile
+  const int64_t col_tiles = (p.N + col_tile - 1) / col_tile;
+  // Pass 2 work-groups and the row steps of each: one column tile sweeping every row
+  // of the group's query heads, or (causal, d = 64) a pair of tiles p and n - 1 - p
+  // sweeping the rows from each tile's first key on, 2 n_stages - 4 (n - 1) steps per
+  // query head for every pair.
+  int64_t units2 = col_tiles * heads_kv;
+  int64_t steps2 = stages * group;
+  if (p.causal) {
+    units2 = (col_tiles + 1) / 2 * heads_kv;
+    steps2 = (col_tiles > 1 ? 2 * stages - 4 * (col_tiles - 1) : stages) * group;
+  }
   // Measured sweep times of one work-group per key (Pass 1) or row step of 64 rows
   // (Pass 2): ~35 and ~74 ns per key, ~3.1 and ~3.7 us per row step at d = 64 / 128.
-  const double sweep1 = (p.d == 64 ? 0.035 : 0.074) * p.N;
   const double sweep2 = (p.d == 64 ? 3.1 : 3.7) * steps2;
-  const double part1 = (double)heads_q * p.N * (4 * p.d + 2) * 4;  // bytes of one part
-  const double part2 = (double)heads_kv * p.N * 2 * p.d * 4;
-  plan.s1 = choose_parts(units1, stages, sweep1, part1);
+  const double part2 = (double)heads_kv * p.N * 2 * p.d * 4;  // bytes of one part
   plan.s2 = choose_parts(units2, steps2, sweep2, part2);
-  if (plan.s1 > 1) {
-    plan.split_keys = (int)((stages + plan.s1 - 1) / plan.s1 * 64);
-    plan.bytes1 = (int64_t)plan.s1 * heads_q * p.N * (4 * p.d + 2) * 4;
+  if (plan.s2 > 1) plan.bytes2 = (int64_t)plan.s2 * heads_kv * p.N * 2 * p.d * 4;
+  // Pass 1 work-groups and their 64-key stages: one row tile of 128 rows sweeping
+  // every key, or (causal, d = 64) row tiles n - 1 - p and p, 2 (n + 1) stages for
+  // every pair when N is a multiple of 128 (the keys up to each tile's last row).
+  const int64_t row_tiles = (p.N + 127) / 128;
+  int64_t units1 = row_tiles * heads_q;
+  int64_t stages1 = stages;
+  if (p.causal) {
+    units1 = (row_tiles + 1) / 2 * heads_q;
+    stages1 = row_tiles > 1 ? stages + 2 : stages;
   }
-  if (plan.s2 > 1) {
-    plan.split_steps = (int)((steps2 + plan.s2 - 1) / plan.s2);
-    plan.bytes2 = (int64_t)plan.s2 * heads_kv * p.N * 2 * p.d * 4;
-  }
+  const double sweep1 = (p.d == 64 ? 0.035 : 0.074) * 64 * stages1;
+  const double part1 = (double)heads_q * p.N * (4 * p.d + 2) * 4;
+  plan.s1 = choose_parts(units1, stages1, sweep1, part1);
+  if (plan.s1 > 1) plan.bytes1 = (int64_t)plan.s1 * heads_q * p.N * (4 * p.d + 2) * 4;
   return plan;
 }
 
@@ -147,7 +166,6 @@ hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass
     a1.part_acc = reinterpret_cast<float*>(ws);
     a1.part_rs = a1.part_acc + (int64_t)plan.s1 * rows * 4 * p.d;
     a1.nsplit = plan.s1;
-    a1.split_keys = plan.split_keys;
     hipError_t e = launch_pass1_split(p, a1, s);
     if (e != hipSuccess) return e;
     const int64_t threads = rows * (p.d / 4);
@@ -171,7 +189,6 @@ hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass
     const int64_t rows = (int64_t)p.B * p.Hkv * p.N;
     a2.part = reinterpret_cast<float*>(ws);  // Pass 1's partials are consumed by now
     a2.nsplit = plan.s2;
-    a2.split_steps = plan.split_steps;
     hipError_t e = launch_pass2_split(p, a2, s);
     if (e != hipSuccess) return e;
     const int64_t threads = rows * (p.d / 4);

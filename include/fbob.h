@@ -175,8 +175,9 @@ int fbob_bob_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64
  * work-groups that write fp32 partial sums to the workspace, and a reduction kernel
  * adds them in a fixed order (results are deterministic; they differ from
  * fbob_bob's only by the order of the fp32 additions) and writes every output once.
- * Splitting applies to bf16 inputs without a causal mask, d = 64 with tau a power of
- * two or d = 128.
+ * Splitting applies to bf16 inputs, d = 64 with tau a power of two or d = 128; with
+ * causal != 0 only at d = 64 and only Pass 2, where a work-group sweeps the rows of
+ * two column tiles (p and n - 1 - p) and the split cuts that joint sweep.
  *   workspace       DEVICE pointer, 16-byte aligned, owned by the caller, at least
  *                   fbob_bob_workspace_size() bytes; NULL (or fewer bytes) runs the
  *                   unsplit schedule, i.e. exactly fbob_bob.  Its contents on entry

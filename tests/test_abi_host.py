@@ -194,12 +194,19 @@ def test_workspace_size_follows_the_split_plan(lib):
     """B=1 H=12 N=4096 d=64: 384 Pass 1 row tiles (1.5 rounds of 256 CUs) split in two
     key parts; Pass 2's 192 column tiles stay whole (four row parts were measured
     slower there: the partial sums cost more than the idle quarter of the CUs), so the
-    workspace holds Pass 1's partials alone.  Problems that fill the GPU, causal ones,
-    fp32 and a tau that is not a power of two at d = 64 need none."""
+    workspace holds Pass 1's partials alone.  With the causal mask only Pass 2 splits,
+    at d = 64: the same shape has 96 work-groups of paired column tiles there, split
+    in two.  Problems that fill the GPU, causal d = 128, fp32 and a tau that is not a
+    power of two at d = 64 need none."""
     heads, N, d = 12, 4096, 64
     assert ws_size(lib) == (OK, 2 * heads * N * (4 * d + 2) * 4)
     assert ws_size(lib, N=16384) == (OK, 0)            # 1536 and 768 tiles: whole rounds
-    assert ws_size(lib, causal=1) == (OK, 0)
+    assert ws_size(lib, causal=1) == (OK, 2 * heads * N * 2 * d * 4)
+    assert ws_size(lib, causal=1, B=4) == (OK, 0)      # partials would cost more
+    assert ws_size(lib, causal=1, d=128, tau=0.125) == (OK, 0)
+    # B=1 H=12 N=16384: 384 tile pairs, 1.5 rounds; two parts fill three whole rounds
+    assert ws_size(lib, causal=1, N=16384) == (OK, 2 * heads * 16384 * 2 * d * 4)
+    assert ws_size(lib, causal=1, N=16384, B=4) == (OK, 0)
     assert ws_size(lib, dtype=0) == (OK, 0)
     assert ws_size(lib, tau=0.1) == (OK, 0)
     # d = 128, grouped heads: Pass 2 splits the (head, row) steps of each K/V tile

@@ -27,6 +27,7 @@ def small(name, B, H, N, d, seed, causal=False):
 CALLS = [
     workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"],   # 96.75 MiB of partial sums
     small("noalloc_n1000_h2_ragged", 1, 2, 1000, 64, 71),      # 15.75 MiB, 8 + 8 parts
+    small("noalloc_causal_n600_h2", 1, 2, 600, 64, 73, causal=True),  # 4.7 MiB, Pass 1 in 4
 ]
 
 
@@ -54,29 +55,31 @@ def assert_same(got, ref, name):
 
 
 def test_noalloc_matches_bob_ws_on_two_calls_in_a_row():
+    """Calls in a row, each smaller than the one before (the scratch keeps the previous
+    call's partial sums), the last one causal."""
     import torch
     import exact_softmax_attention_fbob_amd as fb
     sizes = []
     for w in CALLS:
-        U.say(f"[noalloc] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d}")
+        U.say(f"[noalloc] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
         args, O, L, D = prepared(w)
-        need = fb.bob_workspace_size(args[0], args[1], w.tau)
+        need = fb.bob_workspace_size(args[0], args[1], w.tau, w.causal)
         assert 0 < need <= 128 << 20, need
         sizes.append(need)
         ws = torch.empty(need, dtype=torch.uint8, device=args[0].device)
-        ref = fb.bob_ws(*args, O, L, D, w.tau, workspace=ws)
+        ref = fb.bob_ws(*args, O, L, D, w.tau, w.causal, workspace=ws)
         out = outputs_like(ref)
-        got = fb.bob_noalloc(*args, O, L, D, w.tau, out=out)
+        got = fb.bob_noalloc(*args, O, L, D, w.tau, w.causal, out=out)
         torch.cuda.synchronize()
         assert got is out
         assert_same(got, ref, w.name)
-    assert sizes[1] < sizes[0]
+    assert sizes[2] < sizes[1] < sizes[0]
 
 
 def test_noalloc_without_split_equals_fbob_bob():
     import torch
     import exact_softmax_attention_fbob_amd as fb
-    w = small("noalloc_causal_n300_h2", 1, 2, 300, 64, 72, causal=True)
+    w = small("noalloc_causal_n300_h2_d128", 1, 2, 300, 128, 72, causal=True)
     U.say(f"[noalloc] {w.name} (no split)")
     args, O, L, D = prepared(w)
     assert fb.bob_workspace_size(args[0], args[1], w.tau, True) == 0
