@@ -517,6 +517,80 @@ def causal_ab(args):
     print(_json.dumps(out), flush=True)
 
 
+def graph_timed(fn, reps):
+    """Mean time in us of one call of ``fn``, timed as a HIP graph that replays ``reps``
+    back-to-back calls (one warm-up replay first), so that host-side launch overhead
+    never counts, however short the call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+
+    def run():
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    return run
+
+
+def causal_split(args):
+    """The split schedule on causal problems (d = 64, bf16): fbob_bob against fbob_bob_ws
+    with the workspace the planner asks for, each timed as a HIP graph of back-to-back
+    calls, interleaved over three rounds (median).  Small causal problems leave most CUs
+    idle: one work-group per pair of tiles.  One JSON line per shape; the non-causal
+    GPT-2-heads shape is included for comparison."""
+    import json as _json
+    import statistics
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    import workloads
+    base = workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"]
+    shapes = ((1, 12, 4096, True), (1, 12, 4096, False), (1, 4, 4096, True),
+              (1, 12, 2048, True), (1, 12, 1024, True), (1, 12, 16384, True),
+              (2, 12, 8192, True), (4, 12, 4096, True), (8, 12, 1024, True))
+    for (B, H, N, causal) in shapes:
+        w = base.with_(B=B, H=H, N=N, causal=causal, name=f"b{B}_h{H}_n{N}")
+        print(f"[causal-split] B={B} H={H} N={N} causal={causal}", file=sys.stderr, flush=True)
+        T = {k: torch.from_numpy(v).cuda().to(torch.bfloat16)
+             for k, v in workloads.make_inputs(w).items()}
+        a7 = tuple(T[k] for k in workloads.TENSORS)
+        O, L, D = fb.forward(*a7[:4], w.tau, causal)
+        need = fb.bob_workspace_size(a7[0], a7[1], w.tau, causal)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        reps = max(4, min(50, int(4e5 * 12 * 4096 / (B * H * N * N))))
+        unsplit = graph_timed(lambda: fb.bob(*a7, O, L, D, w.tau, causal), reps)
+        split = graph_timed(lambda: fb.bob_ws(*a7, O, L, D, w.tau, causal, workspace=ws), reps)
+        tu, ts = [], []
+        for _ in range(3):
+            tu.append(unsplit())
+            ts.append(split())
+        u, sp = statistics.median(tu), statistics.median(ts)
+        flops = 38.0 * (N * (N + 1) / 2 if causal else N * N) * w.d * B * H
+        print(_json.dumps({"B": B, "H": H, "N": N, "d": w.d, "causal": causal,
+                           "workspace_bytes": need, "graph_reps": reps,
+                           "bob_us": round(u, 1), "bob_ws_us": round(sp, 1),
+                           "speedup": round(u / sp, 3),
+                           "bob_tflops": round(flops / u / 1e6, 1),
+                           "bob_ws_tflops": round(flops / sp / 1e6, 1)}), flush=True)
+        del T, a7, O, L, D, ws, unsplit, split
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,6 +609,8 @@ def main():
                     help="time the passes at N=4096 d=64 for 2..24 heads (GPU fill level)")
     ap.add_argument("--causal-ab", action="store_true",
                     help="causal B=4 vs non-causal B=2 at H=12 N=16384 d=64, interleaved")
+    ap.add_argument("--causal-split", action="store_true",
+                    help="fbob_bob vs fbob_bob_ws on causal d=64 shapes (HIP-graph timing)")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
     ap.add_argument("--max-n-rows", type=int, default=16,
                     help="rows per length checked against the fp64 oracle in the max-N sweep")
@@ -571,6 +647,13 @@ def main():
             sys.exit(3)
         fb.load_library()
         causal_ab(args)
+        return
+    if args.causal_split:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(3)
+        fb.load_library()
+        causal_split(args)
         return
 
     name = args.workload or workloads.HEADLINE
