@@ -261,9 +261,22 @@ struct MultiStager {
 // block times the row pitch plus the swizzled chunk); tensor bases, block rows
 // and LDS offsets are wave-uniform.  A stage that lies wholly inside the tensor
 // is addressed as uniform base + lane offset; only a stage that crosses the end
-// takes the per-lane clamp.
+// takes the per-lane clamp.  With RFL the uniform part is read from the first lane
+// into scalar registers before the lane offset is added: the compiler otherwise
+// keeps base + lane offset as a 64-bit per-lane address for the whole sweep (two
+// registers per instruction instead of one), which pushed the d = 128 row pass into
+// spills (a reload at every stage, ~3.6 % of its time).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int ROWS, int NT, int NW, bool ASM_DMA = false>
+
+// A wave-uniform pointer, taken from the first lane.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+template <typename T, int D, int ROWS, int NT, int NW, bool ASM_DMA = false, bool RFL = false>
 struct DirectStager {
   static constexpr int kRB = Tile<T, D>::kRowBytes;
   static constexpr int kChunks = Tile<T, D>::kChunks;
@@ -323,8 +336,8 @@ struct DirectStager {
     if (row0 + ROWS <= nrows) {  // wave-uniform: the whole stage lies inside the tensor
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const char* gp = base[k] + byte_off + (int64_t)(row0 + row_blk[k]) * kRB + voff[k];
-        dma(gp, tiles + lds_off[k]);
+        const char* ub = base[k] + byte_off + (int64_t)(row0 + row_blk[k]) * kRB;
+        dma((RFL ? uniform_ptr(ub) : ub) + voff[k], tiles + lds_off[k]);
       }
     } else {
 #pragma unroll

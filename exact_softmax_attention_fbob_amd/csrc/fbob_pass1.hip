@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void pass1_kernel(Pass1Args a, int Hq, int
 
     // Staging: registers + ds_write (MultiStager) or direct global -> LDS.
     using RegStager = MultiStager<T, D, kBC, 4, kThreads>;
-    using DirStager = DirectStager<T, D, kBC, 4, NW>;
+    using DirStager = DirectStager<T, D, kBC, 4, NW, false, (D >= 128)>;
     typename std::conditional<DIRECT, DirStager, RegStager>::type st;
     auto stage_init = [&]() {
       if constexpr (DIRECT) st.init(kv_bases, w, lane);
