@@ -14,7 +14,9 @@
 // Both kernels reuse the layouts of the BoB passes: score tiles computed with
 // the contracted index on the MFMA row axis so that their C registers are the B
 // operand of the following contraction, dP - D obtained by seeding the dP
-// accumulator with -D, staged tiles read back with the swizzled LDS readers.
+// accumulator with -D, staged tiles read back with the swizzled LDS readers, and
+// the wave priority raised while a wave issues its contraction MFMAs (the other
+// wave of the SIMD fills the gaps with its exp and elementwise work).
 
 #include <type_traits>
 
@@ -135,13 +137,14 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
         for (int q = 0; q < 4; ++q) ds[ib][4 * jb + q] = (T)(p[q] * t[ib][q]);
       }
     }
-    FBOB_SCHED_FENCE();
+    FBOB_PRIO_HIGH();
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
       const F kt = rd.tr(Kt, db);
 #pragma unroll
       for (int ib = 0; ib < NI; ++ib) accX[ib][db] = E::mma(kt, ds[ib], accX[ib][db]);
     }
+    FBOB_PRIO_LOW();
   };
 
   using RegStager = MultiStager<T, D, BC, 2, kThreads>;
@@ -261,9 +264,17 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
   // The raw L and D stay in registers until store_step: deriving the seeds here
   // would make this wave wait for every load it has in flight (the tiles'
   // included) before it computes the current stage.
-  auto load_step = [&](int step, char* buf) {
-    const int hq = step / nrc;
-    const int i0 = i_begin + (step % nrc) * BRS;
+  // Steps run in order: the next one to load is query head ld_hq, row chunk ld_rc
+  // (advanced by one chunk per load rather than divided out of the step index).
+  int ld_hq = 0, ld_rc = 0, nxt_i0 = 0;
+  auto load_step = [&](char* buf) {
+    const int hq = ld_hq;
+    const int i0 = i_begin + ld_rc * BRS;
+    nxt_i0 = i0;
+    if (++ld_rc == nrc) {
+      ld_rc = 0;
+      ++ld_hq;
+    }
     if constexpr (DIRECT) st.load(buf, i0, N, hq * q_head);
     else st.load(i0, N, hq * q_head);
     if (tid < BRS) {
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
         }
       }
     }
-    FBOB_SCHED_FENCE();
+    FBOB_PRIO_HIGH();
     const char* Qs = Qt + 32 * sc * Tile<T, D>::kRowBytes;
     const char* dOs = dOt + 32 * sc * Tile<T, D>::kRowBytes;
 #pragma unroll
@@ -343,16 +354,18 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
         accV[jb][db] = E::mma(dot, pB[jb], accV[jb][db]);
       }
     }
+    FBOB_PRIO_LOW();
   };
 
-  load_step(0, lds[0]);
+  load_step(lds[0]);
   if constexpr (DIRECT) wait_all_memory();
   store_step(lds[0]);
   __syncthreads();
+  int cur_i0 = nxt_i0;
   auto step = [&](int t, char* cur, char* nxt) {
-    const int i0 = i_begin + (t % nrc) * BRS;
+    const int i0 = cur_i0;
     const bool more = t + 1 < nsteps;
-    if (more) load_step(t + 1, nxt);
+    if (more) load_step(nxt);
 #pragma unroll
     for (int sc = 0; sc < BRS / 32; ++sc) {
       const bool active = !CAUSAL || i0 + 32 * sc + 31 >= jw0;
@@ -363,6 +376,7 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
     if constexpr (DIRECT) wait_all_memory();
     if (more) store_step(nxt);
     __syncthreads();
+    cur_i0 = nxt_i0;
   };
 #pragma unroll 1
   for (int t = 0; t < nsteps; t += 2) {
