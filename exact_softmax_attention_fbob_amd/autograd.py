@@ -11,7 +11,9 @@
   Phi = <dQ,U_Q> + <dK,U_K> + <dV,U_V> with respect to (Q, K, V, dO), which is
   exactly the BoB of ``fbob_bob`` (FlashBoB notes, "整体框架").  This is what a
   Hessian-vector product through attention needs (the notes' Sophia-H
-  integration: the gradient of <grad L, u> for a random direction u).
+  integration: the gradient of <grad L, u> for a random direction u).  It runs
+  through ``fbob_bob_ws`` with a workspace from torch's allocator, so problems too
+  small to fill the GPU take the split schedule (the others run ``fbob_bob``).
 
 This module is an integration layer above the C ABI and uses torch autograd; the
 arithmetic runs in the library's HIP kernels.  Conventions:
@@ -32,7 +34,7 @@ from __future__ import annotations
 import torch
 
 from . import backward as _backward
-from . import bob as _bob
+from . import bob_ws as _bob_ws
 from . import forward as _forward
 
 __all__ = ["attention"]
@@ -62,7 +64,8 @@ class _AttentionBackward(torch.autograd.Function):
         def cot(u, like):
             return torch.zeros_like(like) if u is None else _contig(u.to(dt))
 
-        r = _bob(Q, K, V, dO, cot(UQ, Q), cot(UK, K), cot(UV, V), O, L, D, ctx.tau, ctx.causal)
+        r = _bob_ws(Q, K, V, dO, cot(UQ, Q), cot(UK, K), cot(UV, V), O, L, D, ctx.tau,
+                    ctx.causal)
         return (r["dQt"].to(dt), r["dKt"].to(dt), r["dVt"].to(dt), r["ddOt"].to(dt),
                 None, None, None, None)
 

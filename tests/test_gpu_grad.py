@@ -205,6 +205,8 @@ AUTOGRAD_CASES = [
     case("ag_n200_h2_bf16", 1, 2, 200, 64, "bf16", 61),
     case("ag_n130_f32_causal", 1, 1, 130, 64, "f32", 62, causal=True),
     case("ag_gqa_hq4_hkv2_n96_d128_bf16_causal", 1, 4, 96, 128, "bf16", 63, causal=True, Hkv=2),
+    # small enough that the double backward takes the split schedule (Pass 1 in 4 parts)
+    case("ag_n600_h2_bf16_causal_split", 1, 2, 600, 64, "bf16", 65, causal=True),
 ]
 
 
