@@ -28,8 +28,18 @@ constexpr float kSlack = 8.0f;  // log2 headroom before the reference max is rai
 
 // PRIO: raise the wave priority while the P V contraction MFMAs issue.
 // NI: 16-row blocks per wave.
+// Waves per SIMD the compiler must allow: the bf16 d = 64 kernel with tau not a power of
+// two (tau applied in the exp2 argument) left alone takes 130 registers, i.e. three waves
+// per SIMD and one eight-wave work-group per CU; held to four it fits 126 with no spill
+// (8 % faster).
+template <typename T, int D, int NW, int BC, bool TP2, bool CAUSAL>
+constexpr int fwd_waves_per_simd() {
+  return D < 128 && sizeof(T) == 2 && !TP2 ? 4 : 1;
+}
+
 template <typename T, int D, int NW, int BC, bool TP2, bool CAUSAL, bool PRIO = false, int NI = 1>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int group, int N,
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd<T, D, NW, BC, TP2, CAUSAL>()))) void fwd_kernel(FwdArgs a, int Hq, int group, int N,
                                                       float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
   using F = typename E::frag;
@@ -167,6 +177,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
   wait_all_memory();
   __syncthreads();
 
+  // Causal: a 32-key block past the wave's last row is masked whole.  Skipping it
+  // saves little (the stage barrier waits for the wave with the most keys anyway),
+  // and at d = 64 the branch around the block costs 44 registers, i.e. half the
+  // occupancy (one work-group per CU instead of two), so there it is computed and
+  // masked (its weights are exactly 0).
+  constexpr bool kSkipMasked = CAUSAL && !(D < 128 && std::is_same<T, __bf16>::value);
   auto step = [&](int t, char* cur, char* nxt) {
     const int j0 = t * BC;
     const bool more = t + 1 < ntc;
@@ -174,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a, int Hq, int gro
 #pragma unroll
     for (int hs = 0; hs < BC / 32; ++hs) {
       const int js = j0 + 32 * hs;
-      if (!CAUSAL || js <= iw0 + kRW - 1)
+      if (!kSkipMasked || js <= iw0 + kRW - 1)
         block32(cur + 32 * hs * Tile<T, D>::kRowBytes,
                 cur + kTB + 32 * hs * Tile<T, D>::kRowBytes, js);
     }
