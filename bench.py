@@ -591,6 +591,55 @@ def causal_split(args):
         torch.cuda.empty_cache()
 
 
+def n_sweep(args):
+    """BoB rate against sequence length at the headline's heads and head size (B=1, H=12,
+    d=64, bf16, non-causal, inputs as the GPT-2-heads recipe): N = 1024 .. 65536.  Each
+    length times fbob_bob and fbob_bob_ws (the workspace the planner asks for, or none)
+    as HIP graphs of back-to-back calls, interleaved over three rounds (median), and reads
+    the engine clock of the sustained load.  One JSON line per length."""
+    import json as _json
+    import statistics
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    import workloads
+    base = workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"]
+    for N in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+        w = base.with_(N=N, name=f"h12_n{N}_d64")
+        print(f"[n-sweep] N={N}", file=sys.stderr, flush=True)
+        T = {k: torch.from_numpy(v).cuda().to(torch.bfloat16)
+             for k, v in workloads.make_inputs(w).items()}
+        a7 = tuple(T[k] for k in workloads.TENSORS)
+        O, L, D = fb.forward(*a7[:4], w.tau)
+        need = fb.bob_workspace_size(a7[0], a7[1], w.tau)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        reps = max(2, min(50, int(50 * (4096 / N) ** 2)))
+        unsplit = graph_timed(lambda: fb.bob(*a7, O, L, D, w.tau), reps)
+        split = graph_timed(lambda: fb.bob_ws(*a7, O, L, D, w.tau, workspace=ws), reps)
+        tu, ts = [], []
+        for _ in range(3):
+            tu.append(unsplit())
+            ts.append(split())
+        u, sp = statistics.median(tu), statistics.median(ts)
+        with ClockSampler() as clk:
+            t_end = time.perf_counter() + 1.0
+            while time.perf_counter() < t_end:
+                unsplit()
+        mhz = clk.result().get("xcd_mean")
+        flops = 38.0 * N * N * w.d * w.H
+        best = min(u, sp)
+        out = {"N": N, "B": 1, "H": 12, "d": 64, "workspace_bytes": need, "graph_reps": reps,
+               "bob_us": round(u, 1), "bob_ws_us": round(sp, 1),
+               "bob_tflops": round(flops / u / 1e6, 1),
+               "best_pct_bf16_peak": round(100 * flops / best / 1e6 / PEAK_TFLOPS["bf16"], 2),
+               "sclk_mhz_measured": mhz}
+        if mhz:
+            out["best_frac_at_measured_sclk"] = round(
+                flops / best / 1e6 / (PEAK_TFLOPS["bf16"] * mhz / SPEC_SCLK_MHZ), 4)
+        print(_json.dumps(out), flush=True)
+        del T, a7, O, L, D, ws, unsplit, split
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -611,6 +660,8 @@ def main():
                     help="causal B=4 vs non-causal B=2 at H=12 N=16384 d=64, interleaved")
     ap.add_argument("--causal-split", action="store_true",
                     help="fbob_bob vs fbob_bob_ws on causal d=64 shapes (HIP-graph timing)")
+    ap.add_argument("--n-sweep", action="store_true",
+                    help="BoB rate against N at B=1 H=12 d=64 (HIP-graph timing)")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
     ap.add_argument("--max-n-rows", type=int, default=16,
                     help="rows per length checked against the fp64 oracle in the max-N sweep")
@@ -654,6 +705,13 @@ def main():
             sys.exit(3)
         fb.load_library()
         causal_split(args)
+        return
+    if args.n_sweep:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(3)
+        fb.load_library()
+        n_sweep(args)
         return
 
     name = args.workload or workloads.HEADLINE

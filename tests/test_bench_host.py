@@ -101,7 +101,8 @@ def test_cpu_baseline_on_a_tiny_workload():
     assert r["extrapolated_full_bob_s"] > 0
 
 
-@pytest.mark.parametrize("mode", [["--fill-sweep"], ["--causal-ab"], ["--causal-split"], ["--max-n"],
+@pytest.mark.parametrize("mode", [["--fill-sweep"], ["--causal-ab"], ["--causal-split"], ["--n-sweep"],
+                                  ["--max-n"],
                                   ["--workspace", "--workload", "gpt2_heads_h12_n4096_d64_bf16"]])
 def test_measurement_modes_parse_and_need_a_gpu(mode):
     """Each measurement mode parses its arguments and, without a visible GPU, stops with
