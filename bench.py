@@ -414,28 +414,19 @@ def fill_sweep(args):
     """How fast one tile sweep runs as a function of how many CUs are busy: the
     GPT-2-heads shape (B=1, N=4096, d=64, bf16) at H = 2 .. 24 heads, i.e. 32 H Pass 1
     row tiles and 16 H Pass 2 column tiles for 256 CUs (one work-group per CU).
-    Each head count times Pass 1 and Pass 2 (HIP events, mean of at least 400 calls
-    after --warmup) and fbob_bob_ws where the split schedule applies.  One JSON line
-    per head count.  (No clock column: the GPU metrics refresh too slowly for windows
-    this short.)"""
+    Each head count times Pass 1, Pass 2 and fbob_bob_ws where the split schedule
+    applies, each as a HIP graph of back-to-back calls (medians of three replays), so
+    that host launch overhead does not count.  One JSON line per head count.  (No clock
+    column: the GPU metrics refresh too slowly for windows this short.)"""
     import json as _json
+    import statistics
     import torch
     import exact_softmax_attention_fbob_amd as fb
     import workloads
     base = workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"]
-    steps, warm = max(args.steps, 400), max(args.warmup, 2)
 
-    def timed(fn):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps * 1e3  # us
+    def med(run):
+        return statistics.median(run() for _ in range(3))
 
     for H in (2, 4, 6, 8, 12, 16, 24):
         w = base.with_(H=H, name=f"gpt2_shape_h{H}")
@@ -445,13 +436,15 @@ def fill_sweep(args):
         args7 = tuple(T[k] for k in workloads.TENSORS)
         O, L, D = fb.forward(*args7[:4], w.tau)
         p1 = fb.bob_pass1(*args7, O, L, D, w.tau)
-        t1 = timed(lambda: fb.bob_pass1(*args7, O, L, D, w.tau))
-        t2 = timed(lambda: fb.bob_pass2(*args7, L, D, p1["alpha"], p1["E"], w.tau))
+        reps = max(10, int(200 * 12 / H))
+        t1 = med(graph_timed(lambda: fb.bob_pass1(*args7, O, L, D, w.tau), reps))
+        t2 = med(graph_timed(lambda: fb.bob_pass2(*args7, L, D, p1["alpha"], p1["E"], w.tau),
+                             reps))
         need = fb.bob_workspace_size(args7[0], args7[1], w.tau)
         tws = None
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-            tws = timed(lambda: fb.bob_ws(*args7, O, L, D, w.tau, workspace=ws))
+            tws = med(graph_timed(lambda: fb.bob_ws(*args7, O, L, D, w.tau, workspace=ws), reps))
         print(_json.dumps({"H": H, "pass1_tiles": 32 * H, "pass1_us": round(t1, 1),
                            "pass2_tiles": 16 * H, "pass2_us": round(t2, 1),
                            "bob_ws_us": None if tws is None else round(tws, 1),
