@@ -207,6 +207,12 @@ def test_workspace_size_follows_the_split_plan(lib):
     # B=1 H=12 N=16384: 384 tile pairs, 1.5 rounds; two parts fill three whole rounds
     assert ws_size(lib, causal=1, N=16384) == (OK, 2 * heads * 16384 * 2 * d * 4)
     assert ws_size(lib, causal=1, N=16384, B=4) == (OK, 0)
+    # B=1 H=4 N=4096: 64 Pass 1 work-groups (16 row-tile pairs x 4 heads) and 32 Pass 2
+    # work-groups for 256 CUs: Pass 1 in four parts, Pass 2 in eight; the workspace
+    # holds the larger of the two sets of partials (the passes reuse it in turn)
+    p1 = 4 * 4 * 4096 * (4 * d + 2) * 4
+    p2 = 8 * 4 * 4096 * 2 * d * 4
+    assert ws_size(lib, causal=1, Hq=4, Hkv=4) == (OK, max(p1, p2))
     assert ws_size(lib, dtype=0) == (OK, 0)
     assert ws_size(lib, tau=0.1) == (OK, 0)
     # d = 128, grouped heads: Pass 2 splits the (head, row) steps of each K/V tile
