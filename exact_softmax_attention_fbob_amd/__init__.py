@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
     bob_pass2(..., alpha, E)                        -> dict(dKt, dVt)
     bob_ws(..., workspace)                          -> as bob; small problems split
     bob_workspace_size(Q, K, tau, causal)           -> bytes bob_ws can use
+    bob_ex(..., flags, workspace)                   -> as bob_ws, with FLAG_* options
+    bob_noalloc(..., out)                           -> as bob_ws, static scratch
 Shapes: Q, dO, U_Q: [B, Hq, N, d]; K, V, U_K, U_V: [B, Hkv, N, d]; L, D, alpha,
 E: [B, Hq, N]; all outputs float32.  ``autograd.attention`` wraps forward,
 backward and bob as a twice-differentiable torch operation.
@@ -28,8 +30,12 @@ import os
 
 from ._lib import FbobError, load_library, STATUS  # noqa: F401
 
-__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "bob_ws", "bob_noalloc",
-           "bob_workspace_size", "load_library", "FbobError", "library_path", "version"]
+__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "bob_ws", "bob_ex",
+           "bob_noalloc", "bob_workspace_size", "FLAG_FP32_ROW_SUMS", "load_library",
+           "FbobError", "library_path", "version"]
+
+# fbob_bob_ex option bits (include/fbob.h): bf16 d = 64 row sums alpha, E' in fp32
+FLAG_FP32_ROW_SUMS = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -238,6 +244,19 @@ def bob_ws(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, workspace=N
     fill the GPU split their sweeps over more work-groups.  ``workspace`` is a
     contiguous GPU tensor of at least ``bob_workspace_size`` bytes (any dtype); None
     allocates one with torch.  Returns the same dict as ``bob``."""
+    return _bob_ws_call("fbob_bob_ws", (), Q, K, V, dO, UQ, UK, UV, O, L, D, tau, causal,
+                        workspace)
+
+
+def bob_ex(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, flags=0, workspace=None):
+    """``bob_ws`` with option bits (C ABI ``fbob_bob_ex``): ``flags`` is an OR of the
+    ``FLAG_*`` values; ``FLAG_FP32_ROW_SUMS`` has Pass 1 sum alpha and E' in fp32 from
+    the unrounded products (bf16 inputs at d = 64; elsewhere it changes nothing)."""
+    return _bob_ws_call("fbob_bob_ex", (int(flags),), Q, K, V, dO, UQ, UK, UV, O, L, D, tau,
+                        causal, workspace)
+
+
+def _bob_ws_call(name, extra, Q, K, V, dO, UQ, UK, UV, O, L, D, tau, causal, workspace):
     torch = _torch()
     lib = load_library()
     B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO, UQ, UK, UV)
@@ -255,7 +274,8 @@ def bob_ws(Q, K, V, dO, UQ, UK, UV, O, L, D, tau=None, causal=False, workspace=N
                ddOt=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
                alpha=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
                E=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
-    _call(dev, lib.fbob_bob_ws, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d), int(bool(causal)),
+    _call(dev, getattr(lib, name), _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), *extra,
           _p(Q), _p(K), _p(V), _p(dO), _p(UQ), _p(UK), _p(UV), _p(O), _p(L), _p(D),
           _p(out["dQt"]), _p(out["dKt"]), _p(out["dVt"]), _p(out["ddOt"]),
           _p(out["alpha"]), _p(out["E"]), _p(workspace), nbytes, _stream(dev))

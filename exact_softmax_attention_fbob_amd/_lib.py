@@ -14,7 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 STATUS = {0: "FBOB_OK", 1: "FBOB_ERR_INVALID_ARG", 2: "FBOB_ERR_UNSUPPORTED",
-          3: "FBOB_ERR_ALIGNMENT", 4: "FBOB_ERR_ALIAS", 5: "FBOB_ERR_HIP"}
+          3: "FBOB_ERR_ALIGNMENT", 4: "FBOB_ERR_ALIAS", 5: "FBOB_ERR_HIP",
+          6: "FBOB_ERR_SCRATCH"}
 
 # Every symbol declared in include/fbob.h, with its ctypes prototype.
 _i64, _f, _i, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
@@ -28,6 +29,7 @@ PROTOTYPES = {
     "fbob_bob_workspace_size": (_i, _SIZES + [ctypes.POINTER(_i64)]),
     "fbob_bob_ws": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp, _i64] + [_vp]),
     "fbob_bob_noalloc": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp]),
+    "fbob_bob_ex": (_i, _SIZES + [_i] + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp, _i64] + [_vp]),
     "fbob_strerror": (ctypes.c_char_p, [_i]),
     "fbob_version": (_i, []),
 }

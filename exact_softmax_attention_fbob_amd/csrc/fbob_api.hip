@@ -256,10 +256,22 @@ int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_
                 const void* UQ, const void* UK, const void* UV, const float* O, const float* L,
                 const float* D, float* dQt, float* dKt, float* dVt, float* ddOt, float* alpha,
                 float* E, void* workspace, int64_t workspace_bytes, void* stream) {
+  return fbob_bob_ex(dtype, B, Hq, Hkv, N, d, tau, causal, 0, Q, K, V, dO, UQ, UK, UV, O, L, D,
+                     dQt, dKt, dVt, ddOt, alpha, E, workspace, workspace_bytes, stream);
+}
+
+int fbob_bob_ex(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
+                int causal, int flags, const void* Q, const void* K, const void* V,
+                const void* dO, const void* UQ, const void* UK, const void* UV, const float* O,
+                const float* L, const float* D, float* dQt, float* dKt, float* dVt,
+                float* ddOt, float* alpha, float* E, void* workspace, int64_t workspace_bytes,
+                void* stream) {
   Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
   if (c.status != FBOB_OK) return c.status;
-  if (workspace_bytes < 0) return FBOB_ERR_INVALID_ARG;
+  if (workspace_bytes < 0 || (flags & ~FBOB_FLAG_FP32_ROW_SUMS) != 0) return FBOB_ERR_INVALID_ARG;
   if (c.empty) return FBOB_OK;
+  // only the bf16 d = 64 kernels round the products their row sums are formed from
+  c.p.fp32_row_sums = (flags & FBOB_FLAG_FP32_ROW_SUMS) && c.p.bf16 && c.p.d == 64;
   const fbob::SplitPlan plan = fbob::split_plan(c.p);
   // The split schedule runs only with a workspace that holds its partial sums;
   // otherwise this is fbob_bob.

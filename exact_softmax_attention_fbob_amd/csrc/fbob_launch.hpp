@@ -32,6 +32,8 @@ struct Problem {
   float tau;
   int causal;
   bool bf16;  // storage type of the seven inputs (else fp32)
+  // bf16 at d = 64: Pass 1 sums alpha and E' in fp32 from the unrounded products
+  bool fp32_row_sums = false;
 };
 
 struct FwdArgs {

@@ -499,7 +499,8 @@ hipError_t launch_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT>
+template <typename T, int D, int NW, int NI, int SCHED, int TM, int BC, bool DIRECT,
+          bool VSUM = false>
 hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   constexpr int kBR = NW * 16 * NI;
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
@@ -508,12 +509,12 @@ hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if constexpr (D >= 128) {
     if (p.causal) return hipErrorInvalidValue;  // split_plan masks only at d = 64
   } else if (p.causal) {
-    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true, false, true>),
+    hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true, VSUM, true>),
                        dim3(total), dim3(NW * 64), 0, s, a, p.Hq, p.Hq / p.Hkv, p.N, p.tau,
                        n_row_tiles, total);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false, false, true>),
+  hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, false, VSUM, true>),
                      dim3(total), dim3(NW * 64), 0, s, a, p.Hq, p.Hq / p.Hkv, p.N, p.tau,
                      n_row_tiles, total);
   return hipGetLastError();
@@ -522,9 +523,11 @@ hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
 }  // namespace
 
 // The shipped bf16 variants of launch_pass1 below (d = 64 with tau a power of two, with
-// or without the causal mask; d = 128 without it), in split form; split_plan admits no
-// other problem.
+// or without the causal mask and with either row-sum form; d = 128 without the mask),
+// in split form; split_plan admits no other problem.
 hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t s) {
+  if (p.d == 64 && p.fp32_row_sums)
+    return launch_split_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true, true>(p, a, s);
   if (p.d == 64) return launch_split_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
   return launch_split_t<__bf16, 128, 8, 1, true, kTauValu, 32, true>(p, a, s);
 }
@@ -532,6 +535,11 @@ hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t 
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.bf16) {
     if (p.d == 64) {
+      // fp32 row sums on request: the same layouts with alpha and E' as lane sums
+      if (p.fp32_row_sums) {
+        if (tau_is_pow2(p.tau)) return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true, true>(p, a, s);
+        return launch_t<__bf16, 64, 8, 1, true, kTauValu, 64, true, true>(p, a, s);
+      }
       if (tau_is_pow2(p.tau)) {
 #if FBOB_TUNING
         const int cfg = tune_choice("FBOB_TUNE_P1");
@@ -546,8 +554,6 @@ hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s) {
         if (cfg == 7) return launch_t<__bf16, 64, 4, 2, 0, kTauPow2, 64, true>(p, a, s);
         if (cfg == 8) return launch_t<__bf16, 64, 4, 2, 2, kTauPow2, 64, true>(p, a, s);
         if (cfg == 9) return launch_t<__bf16, 64, 4, 2, 3, kTauPow2, 64, true>(p, a, s);
-        // the default with alpha, E' as fp32 lane sums of the unrounded products
-        if (cfg == 10) return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true, true>(p, a, s);
 #endif
         return launch_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true>(p, a, s);
       }

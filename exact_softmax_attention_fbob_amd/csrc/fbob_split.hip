@@ -171,9 +171,13 @@ hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass
     const int64_t threads = rows * (p.d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
     // split_plan admits bf16 inputs only; the d = 64 split kernel forms alpha by MFMA
-    // (E' from ddO~), the d = 128 one as lane sums (E' summed over the parts)
-    if (p.d == 64)
+    // (E' from ddO~) unless fp32 row sums are asked for, the d = 128 one as lane sums
+    // (E' summed over the parts)
+    if (p.d == 64 && !p.fp32_row_sums)
       hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 64, true>), grid, dim3(256), 0, s, a1,
+                         rows, plan.s1, p.tau);
+    else if (p.d == 64)
+      hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 64, false>), grid, dim3(256), 0, s, a1,
                          rows, plan.s1, p.tau);
     else
       hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 128, false>), grid, dim3(256), 0, s, a1,

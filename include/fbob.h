@@ -176,8 +176,9 @@ int fbob_bob_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64
  * adds them in a fixed order (results are deterministic; they differ from
  * fbob_bob's only by the order of the fp32 additions) and writes every output once.
  * Splitting applies to bf16 inputs, d = 64 with tau a power of two or d = 128; with
- * causal != 0 only at d = 64 and only Pass 2, where a work-group sweeps the rows of
- * two column tiles (p and n - 1 - p) and the split cuts that joint sweep.
+ * causal != 0 only at d = 64, where a work-group of either pass owns two tiles (p and
+ * n - 1 - p, so that every work-group has the same masked work) and the split cuts
+ * the two tiles' joint sweep into equal parts.
  *   workspace       DEVICE pointer, 16-byte aligned, owned by the caller, at least
  *                   fbob_bob_workspace_size() bytes; NULL (or fewer bytes) runs the
  *                   unsplit schedule, i.e. exactly fbob_bob.  Its contents on entry
@@ -222,6 +223,36 @@ int fbob_bob_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, i
                      const float* O, const float* L, const float* D,
                      float* dQt, float* dKt, float* dVt, float* ddOt,
                      float* alpha, float* E, void* stream);
+
+/* Bits of fbob_bob_ex's flags argument. */
+#define FBOB_FLAG_FP32_ROW_SUMS 1
+
+/*
+ * fbob_bob_ws with options: `flags` is a bitwise OR of FBOB_FLAG_* values, and
+ * flags = 0 gives fbob_bob_ws's results bitwise.
+ *   FBOB_FLAG_FP32_ROW_SUMS  (bf16 inputs, d = 64) Pass 1 forms the row sums
+ *     alpha_i = sum_j P_ij F_ij and E'_i = sum_j P_ij dP~'_ij (FlashBoB notes,
+ *     "关键设计" 1, the alpha-free accumulators) as fp32 sums of the unrounded
+ *     products.  Without it alpha is summed from the same bf16-rounded P F that
+ *     feed the ddO~ contraction, and E' is taken as dO_i . ddO~_i: the rounding then
+ *     cancels in ddO~ = ddO~' - alpha o but stays in alpha (relative ~2^-9 of
+ *     sum_j |P_ij F_ij|), and every dK~ and dV~ column takes alpha_i and E_i of each
+ *     row.  With the flag alpha and E carry fp32 rounding only, so dK~ and dV~ improve
+ *     where rows are near one-hot with large F; ddO~ no longer cancels the rounding
+ *     of P F and its error grows by a small factor.  Pass 1 takes a few percent
+ *     longer.  With f32 inputs no product is rounded to bf16, and at d = 128 the row
+ *     sums are always fp32 lane sums: there the flag changes nothing.
+ *   Any other bit: FBOB_ERR_INVALID_ARG, before any HIP call.
+ * Workspace, the other arguments, outputs and errors as fbob_bob_ws.
+ */
+int fbob_bob_ex(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                float tau, int causal, int flags,
+                const void* Q, const void* K, const void* V, const void* dO,
+                const void* UQ, const void* UK, const void* UV,
+                const float* O, const float* L, const float* D,
+                float* dQt, float* dKt, float* dVt, float* ddOt,
+                float* alpha, float* E, void* workspace, int64_t workspace_bytes,
+                void* stream);
 
 /* Static string naming a status code ("unknown status" for other values). */
 const char* fbob_strerror(int status);

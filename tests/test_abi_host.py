@@ -37,8 +37,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["fbob_forward", "fbob_backward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
-         "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_bob_noalloc", "fbob_strerror",
-         "fbob_version"])
+         "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_bob_ex", "fbob_bob_noalloc",
+         "fbob_strerror", "fbob_version"])
     assert sorted(_lib.PROTOTYPES) == declared_functions()
 
 
@@ -244,6 +244,46 @@ def test_bob_ws_validates_the_workspace(lib):
     assert lib.fbob_bob_ws(1, 1, 2, 2, 64, 96, ctypes.c_float(0.125), 0, *ptrs,
                            fb[16], need, ctypes.c_void_p(0)) == UNSUPPORTED
     assert call_bob_ws(lib, fb[16], need, N=0, ptrs=ptrs) == OK
+
+
+def call_bob_ex(lib, flags, N=4096, d=64, ptrs=None, workspace=None, nbytes=0):
+    p = ptrs or [FakeBuffers(16)[k] for k in range(16)]
+    return lib.fbob_bob_ex(1, 1, 12, 12, N, d, ctypes.c_float(0.125), 0, flags, *p[:16],
+                           workspace, nbytes, ctypes.c_void_p(0))
+
+
+def test_bob_ex_validates_its_flags_before_any_hip_call(lib):
+    """fbob_bob_ex: bits other than FBOB_FLAG_FP32_ROW_SUMS are invalid (also on an
+    empty problem); size errors come first; the rest is fbob_bob_ws's validation."""
+    import exact_softmax_attention_fbob_amd as fb_pkg
+    text = open(HEADER).read()
+    assert re.search(r"#define FBOB_FLAG_FP32_ROW_SUMS 1\b", text)
+    assert fb_pkg.FLAG_FP32_ROW_SUMS == 1
+    for bad in (2, 4, 3, -1, 1 << 30):
+        assert call_bob_ex(lib, bad) == INVALID, bad
+        assert call_bob_ex(lib, bad, N=0) == INVALID, bad
+    assert call_bob_ex(lib, 1, d=96) == UNSUPPORTED
+    assert call_bob_ex(lib, 1, N=0) == OK
+    assert call_bob_ex(lib, 0, N=0) == OK
+    fb = FakeBuffers(17)
+    ptrs = [fb[m] for m in range(16)]
+    ptrs[5] = ctypes.c_void_p(0)
+    assert call_bob_ex(lib, 1, ptrs=ptrs) == INVALID
+    ptrs = [fb[m] for m in range(16)]
+    ptrs[13] = ctypes.c_void_p(fb.addrs[12] + 64)                  # ddO~ inside dV~
+    assert call_bob_ex(lib, 1, ptrs=ptrs) == ALIAS
+    need = ws_size(lib)[1]
+    ptrs = [fb[m] for m in range(16)]
+    assert call_bob_ex(lib, 1, ptrs=ptrs, workspace=fb[16], nbytes=-1) == INVALID
+    assert call_bob_ex(lib, 1, ptrs=ptrs, workspace=ctypes.c_void_p(fb.addrs[16] + 8),
+                       nbytes=need) == ALIGN
+
+
+def test_status_names_cover_every_code(lib):
+    assert sorted(_lib.STATUS) == list(range(7))
+    text = open(HEADER).read()
+    for code, name in _lib.STATUS.items():
+        assert f"{name} = {code}" in text, name
 
 
 def test_header_states_the_scratch_size():
