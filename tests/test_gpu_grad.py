@@ -215,8 +215,18 @@ def _oracle_per_head(inp, w, fn):
     return {(b, h): fn(q, k, b, h) for (b, h) in U.head_list(w)}
 
 
-@pytest.mark.parametrize("w", AUTOGRAD_CASES, ids=[x.name for x in AUTOGRAD_CASES])
-def test_autograd_first_and_second_derivatives(w):
+# the second derivative with the fp32 row-sum option on near-one-hot rows (Q, K x 8),
+# unsplit and split
+ROW_SUM_CASES = [
+    case("ag_n200_h2_bf16_qk8_rowsums", 1, 2, 200, 64, "bf16", 30, scale_qk=8.0),
+    case("ag_n600_h2_bf16_causal_split_rowsums", 1, 2, 600, 64, "bf16", 65, causal=True),
+]
+
+
+@pytest.mark.parametrize("w,row_sums", [(x, False) for x in AUTOGRAD_CASES]
+                         + [(x, True) for x in ROW_SUM_CASES],
+                         ids=[x.name for x in AUTOGRAD_CASES + ROW_SUM_CASES])
+def test_autograd_first_and_second_derivatives(w, row_sums):
     """grad of O against dO is the first backward; the gradient of
     Phi = <dQ,U_Q> + <dK,U_K> + <dV,U_V> with respect to (Q, K, V, dO), taken by
     autograd through the first backward, is the BoB."""
@@ -226,7 +236,7 @@ def test_autograd_first_and_second_derivatives(w):
     inp = U.make_inputs(w)
     dev = U.to_device(inp, w.dtype)
     Q, K, V, dO = (dev[n].clone().requires_grad_(True) for n in ("Q", "K", "V", "dO"))
-    O = attention(Q, K, V, w.tau, w.causal)
+    O = attention(Q, K, V, w.tau, w.causal, fp32_row_sums=row_sums)
     gQ, gK, gV = torch.autograd.grad(O, (Q, K, V), grad_outputs=dO, create_graph=True)
     phi = ((gQ.float() * dev["UQ"].float()).sum() + (gK.float() * dev["UK"].float()).sum()
            + (gV.float() * dev["UV"].float()).sum())
