@@ -1,6 +1,7 @@
 """GPU parity on seeded random configurations: combinations of batch, grouped heads,
 length (tiny, ragged, several tiles), head size, mask, tau, input scale and storage
-type that the hand-picked cases do not cover one by one.
+type that the hand-picked cases do not cover one by one.  A second, wider draw of 150
+runs every BoB entry point (the fp32 row-sum option and the static-scratch form too).
 
 Every configuration runs the forward, the BoB (``fbob_bob``, and ``fbob_bob_ws`` with
 the workspace the planner asks for) and the first backward through the C ABI and
@@ -52,6 +53,37 @@ def random_configs(n=N_CONFIGS, seed=20261203):
 CONFIGS = random_configs()
 
 
+def wide_configs(n=150, seed=777):
+    """A second, wider draw: three K/V heads, groups of four, B up to 3, lengths around
+    every tile boundary up to 1300, tau from 0.05 to 0.3 and Q, K scaled up to x4 (score
+    std up to ~38 at tau 0.3: rows effectively one-hot), U scaled down or up."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for k in range(n):
+        d = int(rng.choice([64, 128]))
+        dtype = "f32" if rng.random() < 0.15 else "bf16"
+        hkv = int(rng.choice([1, 2, 3]))
+        group = int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([1, 2, 3]))
+        lengths = [2, 3, 15, 16, 31, 33, 63, 65, 127, 128, 191, 255, 256, 257, 383, 511, 513]
+        if dtype == "bf16":
+            lengths += [640, 1000, 1023, 1025, 1300]
+        N = int(rng.choice(lengths))
+        causal = bool(rng.random() < 0.5)
+        tau = float(rng.choice([1.0 / np.sqrt(d), 0.125, 0.0625, 0.1, 0.3, 0.05]))
+        scale_qk = float(rng.choice([0.5, 1.0, 2.0, 4.0]))
+        scale_u = float(rng.choice([1.0, 0.1, 3.0]))
+        name = (f"sw{k:03d}_b{B}_hq{hkv * group}_hkv{hkv}_n{N}_d{d}_{dtype}"
+                f"{'_c' if causal else ''}_t{tau:.3f}_qk{scale_qk:g}_u{scale_u:g}")
+        out.append(workloads.Workload(name, B=B, H=hkv * group, N=N, d=d, dtype=dtype,
+                                      seed=9000 + k, causal=causal, scale_qk=scale_qk,
+                                      scale_u=scale_u, extra={"Hkv": hkv, "tau": tau}))
+    return out
+
+
+WIDE = wide_configs()
+
+
 @pytest.mark.parametrize("w", CONFIGS, ids=[w.name for w in CONFIGS])
 def test_random_configuration_matches_oracle(w):
     import torch
@@ -94,5 +126,36 @@ def test_random_configuration_matches_oracle(w):
         errs[kk] = U.rel(np.stack([gd[kk][b, j] for b, j in keys]),
                          np.stack([grads[kk][key] for key in keys]))
     U.say(f"[random] {w.name}: " + " ".join(f"{kk}={v:.1e}" for kk, v in errs.items()))
+    bad = {kk: v for kk, v in errs.items() if not (v <= U.TOL[w.dtype])}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("w", WIDE, ids=[w.name for w in WIDE])
+def test_wide_random_configuration_every_bob_entry_point(w):
+    """fbob_bob, fbob_bob_ws, fbob_bob_ex with fp32 row sums and fbob_bob_noalloc (where
+    the split fits the static scratch) against the oracle, every output element."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    U.say(f"[wide] {w.name}")
+    inp = U.make_inputs(w)
+    dev = U.to_device(inp, w.dtype)
+    a7 = tuple(dev[k] for k in workloads.TENSORS)
+    O, L, D = fb.forward(*a7[:4], w.tau, w.causal)
+    runs = {"bob": fb.bob(*a7, O, L, D, w.tau, w.causal),
+            "ws": fb.bob_ws(*a7, O, L, D, w.tau, w.causal),
+            "ex": fb.bob_ex(*a7, O, L, D, w.tau, w.causal, flags=fb.FLAG_FP32_ROW_SUMS)}
+    if fb.bob_workspace_size(a7[0], a7[1], w.tau, w.causal) <= 128 << 20:
+        runs["noalloc"] = fb.bob_noalloc(*a7, O, L, D, w.tau, w.causal)
+    torch.cuda.synchronize()
+    ref = U.oracle_full(inp, w)
+    errs = {}
+    for kind, out in runs.items():
+        got = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+        got.update(O=O.cpu().numpy().astype(np.float64), L=L.cpu().numpy().astype(np.float64),
+                   D=D.cpu().numpy().astype(np.float64))
+        keys = U.ALL_KEYS + (("O", "L", "D") if kind == "bob" else ())
+        errs.update({f"{kind}.{k}": v for k, v in U.compare_full(got, ref, w, keys=keys).items()})
+    top = max(errs, key=errs.get)
+    U.say(f"[wide] {w.name}: worst {top}={errs[top]:.2e}")
     bad = {kk: v for kk, v in errs.items() if not (v <= U.TOL[w.dtype])}
     assert not bad, bad
