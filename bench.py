@@ -633,6 +633,43 @@ def n_sweep(args):
         torch.cuda.empty_cache()
 
 
+def row_sums(args):
+    """Cost of the fp32 row-sum option (fbob_bob_ex, FBOB_FLAG_FP32_ROW_SUMS) against the
+    default row sums: both through fbob_bob_ex with the workspace the planner asks for,
+    each timed as a HIP graph of back-to-back calls, interleaved over three rounds
+    (median).  One JSON line per shape (bf16, d = 64)."""
+    import json as _json
+    import statistics
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    import workloads
+    shapes = (("h12_n16384_d64_bf16_u01", False), ("gpt2_heads_h12_n4096_d64_bf16", False),
+              ("gpt2_heads_h12_n4096_d64_bf16", True), ("pages_causal_b4_h12_n16384_d64_bf16", True))
+    for wname, causal in shapes:
+        w = workloads.WORKLOADS[wname].with_(causal=causal)
+        print(f"[row-sums] {wname} causal={causal}", file=sys.stderr, flush=True)
+        T = workloads.make_inputs_device(w)
+        a7 = tuple(T[k] for k in workloads.TENSORS)
+        O, L, D = fb.forward(*a7[:4], w.tau, causal)
+        need = fb.bob_workspace_size(a7[0], a7[1], w.tau, causal)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        reps = max(3, min(40, int(40 * 12 * 4096 ** 2 / (w.B * w.H * w.N * w.N))))
+        runs = {f: graph_timed(lambda f=f: fb.bob_ex(*a7, O, L, D, w.tau, causal, flags=f,
+                                                     workspace=ws), reps)
+                for f in (0, fb.FLAG_FP32_ROW_SUMS)}
+        t = {f: [] for f in runs}
+        for _ in range(3):
+            for f, run in runs.items():
+                t[f].append(run())
+        d0, d1 = statistics.median(t[0]), statistics.median(t[fb.FLAG_FP32_ROW_SUMS])
+        print(_json.dumps({"workload": wname, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                           "causal": causal, "workspace_bytes": need, "graph_reps": reps,
+                           "default_us": round(d0, 1), "fp32_row_sums_us": round(d1, 1),
+                           "cost": round(d1 / d0 - 1, 4)}), flush=True)
+        del T, a7, O, L, D, ws, runs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -655,6 +692,8 @@ def main():
                     help="fbob_bob vs fbob_bob_ws on causal d=64 shapes (HIP-graph timing)")
     ap.add_argument("--n-sweep", action="store_true",
                     help="BoB rate against N at B=1 H=12 d=64 (HIP-graph timing)")
+    ap.add_argument("--row-sums", action="store_true",
+                    help="cost of fbob_bob_ex's fp32 row sums against the default (HIP graphs)")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
     ap.add_argument("--max-n-rows", type=int, default=16,
                     help="rows per length checked against the fp64 oracle in the max-N sweep")
@@ -705,6 +744,13 @@ def main():
             sys.exit(3)
         fb.load_library()
         n_sweep(args)
+        return
+    if args.row_sums:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(3)
+        fb.load_library()
+        row_sums(args)
         return
 
     name = args.workload or workloads.HEADLINE
