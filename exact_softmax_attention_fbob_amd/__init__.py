@@ -18,7 +18,8 @@ Entry points (same names as the C ABI):
     bob_ex(..., flags, workspace)                   -> as bob_ws, with FLAG_* options
     bob_noalloc(..., out)                           -> as bob_ws, static scratch
 Shapes: Q, dO, U_Q: [B, Hq, N, d]; K, V, U_K, U_V: [B, Hkv, N, d]; L, D, alpha,
-E: [B, Hq, N]; all outputs float32.  ``autograd.attention`` wraps forward,
+E: [B, Hq, N]; all outputs float32.  ``FBOB_SYNC_DEBUG=1`` in the environment (read at
+import) makes every call wait for its stream and name itself in a device error.  ``autograd.attention`` wraps forward,
 backward and bob as a twice-differentiable torch operation.
 """
 
@@ -105,11 +106,26 @@ def _stream(dev):
     return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
 
 
+# FBOB_SYNC_DEBUG=1 (read once, at import): after every library call the binding waits
+# for the call's stream, so that an asynchronous device error is reported by the call
+# that launched the faulting kernel (named in the message) instead of by a later one.
+# Debugging aid only: it serialises host and device (and is skipped while the stream is
+# being captured into a HIP graph).  The C library itself reads no environment.
+_SYNC_DEBUG = os.environ.get("FBOB_SYNC_DEBUG", "") not in ("", "0")
+
+
 def _call(dev, fn, *args):
     """Call a library entry point with the inputs' device current (the kernels launch
     on the current device, into the given stream of that device)."""
-    with _torch().cuda.device(dev):
+    torch = _torch()
+    with torch.cuda.device(dev):
         st = fn(*args)
+        if st == 0 and _SYNC_DEBUG and not torch.cuda.is_current_stream_capturing():
+            try:
+                torch.cuda.current_stream(dev).synchronize()
+            except RuntimeError as e:
+                raise RuntimeError(f"{getattr(fn, '__name__', 'fbob call')}: device error "
+                                   f"after launch ({e})") from e
     if st != 0:
         raise FbobError(st)
 

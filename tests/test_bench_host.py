@@ -115,3 +115,14 @@ def test_measurement_modes_parse_and_need_a_gpu(mode):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 3, r.stderr
     assert "no GPU visible" in r.stderr
+
+
+def test_sync_debug_flag_is_read_at_import():
+    """FBOB_SYNC_DEBUG is read by the binding once, at import (no GPU needed)."""
+    code = "import exact_softmax_attention_fbob_amd as fb; print(fb._SYNC_DEBUG)"
+    for val, want in (("1", "True"), ("0", "False"), ("", "False")):
+        env = dict(os.environ, FBOB_SYNC_DEBUG=val)
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                           timeout=300, cwd=ROOT, env=env)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.strip() == want, (val, r.stdout)

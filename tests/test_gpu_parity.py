@@ -377,6 +377,29 @@ def test_runs_on_a_side_stream():
         assert torch.equal(ref[k], got[k]), k
 
 
+def test_sync_debug_mode_gives_the_same_results(monkeypatch):
+    """FBOB_SYNC_DEBUG (the binding waits for the stream after every call) changes no
+    result: forward, BoB and first backward bitwise equal to the asynchronous calls."""
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    w = case("syncdebug_n300_h2_bf16_causal", 1, 2, 300, 64, "bf16", 35, causal=True)
+    U.say(f"[parity] {w.name}")
+    dev = U.to_device(U.make_inputs(w), w.dtype)
+    a7 = tuple(dev[k] for k in workloads.TENSORS)
+
+    def run():
+        O, L, D = fb.forward(*a7[:4], w.tau, w.causal)
+        out = fb.bob(*a7, O, L, D, w.tau, w.causal)
+        g = fb.backward(*a7[:4], O, L, w.tau, w.causal)
+        torch.cuda.synchronize()
+        return {"O": O, "L": L, "D": D, **out, **{"g" + k: v for k, v in g.items()}}
+    ref = run()
+    monkeypatch.setattr(fb, "_SYNC_DEBUG", True)
+    got = run()
+    for k in ref:
+        assert torch.equal(ref[k], got[k]), k
+
+
 def test_hip_graph_capture_and_replay():
     """The library allocates nothing and issues no memset, so forward + BoB can be
     captured in a HIP graph.  New inputs are copied into the captured buffers before
