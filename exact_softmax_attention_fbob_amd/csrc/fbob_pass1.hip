@@ -31,10 +31,13 @@
 // -D, giving dP - D directly), tau is folded into the resident operands of the F
 // tile, and the row sum alpha is an MFMA contraction with a ones operand, which
 // leaves seven VALU operations plus one exp per score element (E' comes from the
-// identity below).  At d = 128 (twice
+// identity above).  At d = 128 (twice
 // the accumulators) the register budget of two waves per SIMD is met by keeping the
 // operands unscaled (tau applied to the F tile on the VALU), taking alpha and E' as
-// lane-local fp32 sums, and keeping one LDS offset per access pattern.
+// lane-local fp32 sums, and keeping one LDS offset per access pattern.  The d = 64
+// kernels take the same lane sums when the caller asks for fp32 row sums (the VSUM
+// form below): alpha then carries no bf16 rounding of P F, and E' is summed over the
+// keys, since the identity above holds for the rounded products only with the MFMA alpha.
 #include <type_traits>
 
 #include "fbob_device.hpp"

@@ -24,6 +24,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -34,11 +35,20 @@ KERNEL_SOURCES = {"pass1_kernel": ("fbob_device.hpp", "fbob_pass1.hip"),
                   "pass2_kernel": ("fbob_device.hpp", "fbob_pass2.hip")}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without /* */ and // comments, blank lines or trailing spaces."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_digest(kernel: str) -> str:
+    """Digest of the kernel's sources with comments, blank lines and trailing spaces
+    removed: a counter record stays valid across comment edits, and only across them."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "exact_softmax_attention_fbob_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_softmax_attention_fbob_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -70,6 +70,16 @@ def test_traffic_record_calibration_and_digest(tmp_path, monkeypatch):
     assert bench.measured_traffic("h12_n16384_d64_bf16_u01") is None
 
 
+def test_source_digest_ignores_comments_only():
+    """The counter records are keyed to the code: comments, blank lines and trailing
+    spaces do not change the digest, any code change does."""
+    a = "int f(int x) {  // doubled\n  return 2 * x; /* why */\n}\n"
+    b = "/* header */\nint f(int x) {\n\n  return 2 * x;   \n}\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b) == profiling._code_only(a)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
 def test_bench_and_profiling_digest_agree():
     """bench.py and the recorder hash the same Pass 1 and Pass 2 sources."""
     for k in ("pass1_kernel", "pass2_kernel"):
