@@ -16,8 +16,8 @@
 //   dS = P t,   ddP = P u,   dS~ = P (u t + g'),
 // and t, u, g' come straight out of the MFMAs by seeding their accumulators with
 // the row scalars -D, -alpha and -(E + alpha D); tau is folded into the resident
-// K and U_K operands of the F tile (at d = 128, where tau is not a power of two,
-// the operands stay unscaled, the F - alpha accumulator is seeded with
+// K and U_K operands of the F tile (when tau is not a power of two, and always at
+// d = 128, the operands stay unscaled, the F - alpha accumulator is seeded with
 // -alpha / tau and scaled by tau on the VALU).  That leaves five VALU operations
 // plus one exp per score element.
 //

@@ -11,8 +11,8 @@
 // the single-sweep epilogue does:
 //   Pass 1 (FlashBoB notes, "关键设计" 1, the affine correction, through R = X + D B):
 //     ddO~ = ddO~' - alpha o,  dQ~ = tau (Omega - alpha X - E' B),  E = E' - alpha D,
-//     with E' = <dO, ddO~> where the split kernel forms alpha by MFMA (d = 64), else
-//     the sum of the parts' E';
+//     with E' = <dO, ddO~> where the split kernel forms alpha by MFMA (d = 64 with the
+//     default row sums), else the sum of the parts' E' (fp32 row sums; d = 128);
 //   Pass 2: dK~ = sum of tau dK~ parts,  dV~ = sum of dV~ parts.
 // Every output is still written exactly once, with no atomics.  With the causal mask
 // (d = 64) a Pass 2 work-group sweeps two column tiles, p and n - 1 - p, whose row
