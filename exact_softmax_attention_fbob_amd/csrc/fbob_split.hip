@@ -151,37 +151,111 @@ SplitPlan split_plan(const Problem& p) {
     stages1 = row_tiles > 1 ? stages + 2 : stages;
   }
   const double sweep1 = (p.d == 64 ? 0.035 : 0.074) * 64 * stages1;
-  const double part1 = (double)heads_q * p.N * (4 * p.d + 2) * 4;
-  plan.s1 = choose_parts(units1, stages1, sweep1, part1);
+  const double row_bytes1 = (double)p.N * (4 * p.d + 2) * 4;  // one head's partials, one part
+  plan.s1 = choose_parts(units1, stages1, sweep1, heads_q * row_bytes1);
   if (plan.s1 > 1) plan.bytes1 = (int64_t)plan.s1 * heads_q * p.N * (4 * p.d + 2) * 4;
+  // Without the mask, when the row tiles fill at least one whole round, the heads of
+  // the whole rounds can run unsplit and only the heads of the last, partly idle round
+  // split (B=1 H=12 N=4096: 8 heads unsplit, 4 in two parts): the same rounds of sweep
+  // time, a third of the partial sums.  The leading heads must be whole groups of
+  // query heads (one batch) or whole batches, so that both parts are problems of
+  // their own.
+  if (!p.causal && units1 >= kCUs && row_tiles <= kCUs) {
+    const int64_t per_round = kCUs / row_tiles;  // heads per round of work-groups
+    const int64_t full = units1 / kCUs * per_round;
+    const int64_t rest = heads_q - full;
+    const bool whole = p.B == 1 ? full % group == 0 : full % p.Hq == 0;
+    if (rest > 0 && whole) {
+      const int s_rest = choose_parts(rest * row_tiles, stages1, sweep1, rest * row_bytes1);
+      const auto est = [&](int64_t units, int s, double bytes) {
+        const double rounds = (double)((units * s + kCUs - 1) / kCUs);
+        return rounds * sweep1 / s + (s > 1 ? 2.0 * s * bytes / 5.0e6 + 5.0 : 0.0);
+      };
+      const double uniform = est(units1, plan.s1, heads_q * row_bytes1);
+      const double partial = (double)(full / per_round) * sweep1 +
+                             est(rest * row_tiles, s_rest, rest * row_bytes1);
+      if (s_rest > 1 && partial < uniform) {
+        plan.s1 = s_rest;
+        plan.full1 = full;
+        plan.bytes1 = (int64_t)s_rest * rest * p.N * (4 * p.d + 2) * 4;
+      }
+    }
+  }
   return plan;
 }
+
+namespace {
+
+// The query heads [h0, h0 + n) of a problem (whole groups of one batch, or whole
+// batches) as a problem of their own, with every pointer moved to head h0.
+void head_range(const Problem& p, const Pass1Args& a, int64_t h0, int64_t n, Problem* sp,
+                Pass1Args* sa) {
+  const int64_t group = p.Hq / p.Hkv;
+  *sp = p;
+  if (p.B == 1) {
+    sp->Hq = (int)n;
+    sp->Hkv = (int)(n / group);
+  } else {
+    sp->B = (int)(n / p.Hq);
+  }
+  const int64_t es = p.bf16 ? 2 : 4;
+  const int64_t q = h0 * p.N * p.d, kv = h0 / group * p.N * p.d, r = h0 * p.N;
+  auto in = [&](const void* x, int64_t off) {
+    return static_cast<const void*>(static_cast<const char*>(x) + off * es);
+  };
+  *sa = a;
+  sa->Q = in(a.Q, q);
+  sa->dO = in(a.dO, q);
+  sa->UQ = in(a.UQ, q);
+  sa->K = in(a.K, kv);
+  sa->V = in(a.V, kv);
+  sa->UK = in(a.UK, kv);
+  sa->UV = in(a.UV, kv);
+  sa->O = a.O + q;
+  sa->L = a.L + r;
+  sa->D = a.D + r;
+  sa->dQt = a.dQt + q;
+  sa->ddOt = a.ddOt + q;
+  sa->alpha = a.alpha + r;
+  sa->E = a.E + r;
+}
+
+}  // namespace
 
 hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass2Args& a2_in,
                             const SplitPlan& plan, void* workspace, hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
   if (plan.s1 > 1) {
+    Problem p1 = p;
     Pass1Args a1 = a1_in;
-    const int64_t rows = (int64_t)p.B * p.Hq * p.N;
+    if (plan.full1 > 0) {  // leading heads unsplit, the rest split below
+      Problem pf;
+      Pass1Args af;
+      head_range(p, a1_in, 0, plan.full1, &pf, &af);
+      const hipError_t e = launch_pass1(pf, af, s);
+      if (e != hipSuccess) return e;
+      head_range(p, a1_in, plan.full1, (int64_t)p.B * p.Hq - plan.full1, &p1, &a1);
+    }
+    const int64_t rows = (int64_t)p1.B * p1.Hq * p1.N;
     a1.part_acc = reinterpret_cast<float*>(ws);
     a1.part_rs = a1.part_acc + (int64_t)plan.s1 * rows * 4 * p.d;
     a1.nsplit = plan.s1;
-    hipError_t e = launch_pass1_split(p, a1, s);
+    hipError_t e = launch_pass1_split(p1, a1, s);
     if (e != hipSuccess) return e;
-    const int64_t threads = rows * (p.d / 4);
+    const int64_t threads = rows * (p1.d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
     // split_plan admits bf16 inputs only; the d = 64 split kernel forms alpha by MFMA
     // (E' from ddO~) unless fp32 row sums are asked for, the d = 128 one as lane sums
     // (E' summed over the parts)
-    if (p.d == 64 && !p.fp32_row_sums)
+    if (p1.d == 64 && !p1.fp32_row_sums)
       hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 64, true>), grid, dim3(256), 0, s, a1,
-                         rows, plan.s1, p.tau);
-    else if (p.d == 64)
+                         rows, plan.s1, p1.tau);
+    else if (p1.d == 64)
       hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 64, false>), grid, dim3(256), 0, s, a1,
-                         rows, plan.s1, p.tau);
+                         rows, plan.s1, p1.tau);
     else
       hipLaunchKernelGGL((reduce_pass1_kernel<__bf16, 128, false>), grid, dim3(256), 0, s, a1,
-                         rows, plan.s1, p.tau);
+                         rows, plan.s1, p1.tau);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {

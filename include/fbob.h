@@ -205,7 +205,7 @@ int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_
  * device it runs on until the process ends; the library allocates nothing and
  * issues no memset (every partial a call reads is written earlier in that call).
  *   * FBOB_ERR_SCRATCH, before any HIP call, if the workspace size exceeds
- *     FBOB_SCRATCH_BYTES (e.g. B=1 H=12 N=4096 d=128 needs ~202 MB); fbob_bob or
+ *     FBOB_SCRATCH_BYTES (e.g. B=1 H=10 N=4096 d=128 needs 160 MiB); fbob_bob or
  *     fbob_bob_ws serve such problems.
  *   * All calls on one device share that device's array: calls that overlap in
  *     time on one device (on different streams, or from threads without an order

@@ -191,15 +191,22 @@ def ws_size(lib, dtype=1, B=1, Hq=12, Hkv=12, N=4096, d=64, tau=0.125, causal=0)
 
 
 def test_workspace_size_follows_the_split_plan(lib):
-    """B=1 H=12 N=4096 d=64: 384 Pass 1 row tiles (1.5 rounds of 256 CUs) split in two
-    key parts; Pass 2's 192 column tiles stay whole (four row parts were measured
-    slower there: the partial sums cost more than the idle quarter of the CUs), so the
-    workspace holds Pass 1's partials alone.  With the causal mask only Pass 2 splits,
-    at d = 64: the same shape has 96 work-groups of paired column tiles there, split
-    in two.  Problems that fill the GPU, causal d = 128, fp32 and a tau that is not a
-    power of two at d = 64 need none."""
+    """B=1 H=12 N=4096 d=64: 384 Pass 1 row tiles (1.5 rounds of 256 CUs); the first 8
+    heads (256 tiles, one whole round) run unsplit and the last 4 split in two key
+    parts, which fill the second round; Pass 2's 192 column tiles stay whole (four row
+    parts were measured slower there: the partial sums cost more than the idle quarter
+    of the CUs), so the workspace holds the 4 heads' Pass 1 partials alone.  With the
+    causal mask only Pass 2 splits, at d = 64: the same shape has 96 work-groups of
+    paired column tiles there, split in two.  Problems that fill the GPU, causal
+    d = 128, fp32 and a tau that is not a power of two at d = 64 need none."""
     heads, N, d = 12, 4096, 64
-    assert ws_size(lib) == (OK, 2 * heads * N * (4 * d + 2) * 4)
+    assert ws_size(lib) == (OK, 2 * 4 * N * (4 * d + 2) * 4)
+    # whole batches unsplit (B=3 H=4: batches 0-1, 256 tiles), the last one in two parts
+    assert ws_size(lib, B=3, Hq=4, Hkv=4) == (OK, 2 * 4 * N * (4 * d + 2) * 4)
+    # the leading part must not cut a group of query heads (3 per K/V head here) or a
+    # batch (6 heads per batch): then every head splits, as before
+    assert ws_size(lib, Hq=12, Hkv=4) == (OK, 2 * heads * N * (4 * d + 2) * 4)
+    assert ws_size(lib, B=2, Hq=6, Hkv=6) == (OK, 2 * heads * N * (4 * d + 2) * 4)
     assert ws_size(lib, N=16384) == (OK, 0)            # 1536 and 768 tiles: whole rounds
     assert ws_size(lib, causal=1) == (OK, 2 * heads * N * 2 * d * 4)
     assert ws_size(lib, causal=1, B=4) == (OK, 0)      # partials would cost more
@@ -300,19 +307,20 @@ def call_bob_noalloc(lib, B=1, Hq=12, Hkv=12, N=4096, d=64, ptrs=None):
 
 def test_bob_noalloc_validates_before_any_hip_call(lib):
     """Errors that need no GPU: sizes, pointers, and a split schedule larger than the
-    static scratch (B=1 H=12 N=4096 d=128: Pass 1 in two parts of 12 x 4096 rows x
-    (4 x 128 + 2) fp32, ~202 MB > 128 MiB)."""
-    st, need = ws_size(lib, N=4096, d=128, tau=1 / 128 ** 0.5)
-    assert st == OK and need > SCRATCH_BYTES
-    assert call_bob_noalloc(lib, d=128) == SCRATCH
-    # the C2 problem fits (its workspace is 96.75 MiB)
+    static scratch (B=1 H=10 N=4096 d=128: Pass 2 in four parts of 10 x 4096 rows x
+    2 x 128 fp32, 160 MiB > 128 MiB)."""
+    st, need = ws_size(lib, Hq=10, Hkv=10, N=4096, d=128, tau=1 / 128 ** 0.5)
+    assert st == OK and need == 4 * 10 * 4096 * 2 * 128 * 4 > SCRATCH_BYTES
+    assert call_bob_noalloc(lib, Hq=10, Hkv=10, d=128) == SCRATCH
+    # the C2 problem fits (its workspace is 32.25 MiB), and so does its d = 128 form
     assert 0 < ws_size(lib)[1] <= SCRATCH_BYTES
+    assert 0 < ws_size(lib, d=128, tau=1 / 128 ** 0.5)[1] <= SCRATCH_BYTES
     assert call_bob_noalloc(lib, d=96) == UNSUPPORTED
     assert call_bob_noalloc(lib, N=0) == OK
     fb = FakeBuffers(16)
     ptrs = [fb[m] for m in range(16)]
     ptrs[3] = ctypes.c_void_p(0)
-    assert call_bob_noalloc(lib, d=128, ptrs=ptrs) == INVALID      # pointers before scratch
+    assert call_bob_noalloc(lib, Hq=10, Hkv=10, d=128, ptrs=ptrs) == INVALID  # before scratch
     ptrs = [fb[m] for m in range(16)]
     ptrs[10] = ctypes.c_void_p(fb.addrs[0])                         # dQ~ on top of Q
-    assert call_bob_noalloc(lib, d=128, ptrs=ptrs) == ALIAS
+    assert call_bob_noalloc(lib, Hq=10, Hkv=10, d=128, ptrs=ptrs) == ALIAS

@@ -2,7 +2,9 @@
 
 With a workspace, problems too small to fill the GPU split each Pass 1 row tile's
 key sweep and each Pass 2 column tile's row sweep over several work-groups, which
-write fp32 partial sums that a reduction kernel adds.  With the causal mask (d = 64)
+write fp32 partial sums that a reduction kernel adds.  Where Pass 1's row tiles fill
+whole rounds of the CUs and leave a partial one, the heads of the whole rounds run
+unsplit and only the rest split (a launch on each head range).  With the causal mask (d = 64)
 a work-group sweeps two tiles (row tiles n - 1 - p and p in Pass 1, column tiles p and
 n - 1 - p in Pass 2), and the split cuts that joint sweep, so a part can end in one
 tile and begin the other.  The outputs are checked against the fp64 oracle (same bars as the unsplit
@@ -42,6 +44,13 @@ SPLIT_CASES = [
     case("split_causal_gqa_hq8_hkv2_n700", 1, 8, 700, 64, "bf16", 67, Hkv=2, causal=True),
     case("split_causal_n2048_b2_h3_qk2", 2, 3, 2048, 64, "bf16", 68, causal=True,
          scale_qk=2.0),                                           # Pass 1 in 4, Pass 2 in 8
+    # Pass 1 unsplit on the heads of whole rounds, split on the rest (384 row tiles: 256
+    # in one round unsplit, 128 in two parts): grouped heads (the unsplit part ends on a
+    # group boundary, the split part starts at K/V head 8), whole batches (batches 0-1
+    # unsplit, batch 2 split), and d = 128 with a ragged N
+    case("split_partial_hq24_hkv12_n2048", 1, 24, 2048, 64, "bf16", 74, Hkv=12),
+    case("split_partial_b3_h8_n2048", 3, 8, 2048, 64, "bf16", 75),
+    case("split_partial_h24_n2000_d128", 1, 24, 2000, 128, "bf16", 76),
 ]
 
 # The GPT-2-heads shape with the causal mask: 96 Pass 2 work-groups (8 tile pairs x 12

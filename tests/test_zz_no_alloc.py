@@ -25,7 +25,7 @@ def small(name, B, H, N, d, seed, causal=False):
 
 
 CALLS = [
-    workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"],   # 96.75 MiB of partial sums
+    workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"],   # 32.25 MiB: 4 heads in 2 parts
     small("noalloc_n1000_h2_ragged", 1, 2, 1000, 64, 71),      # 15.75 MiB, 8 + 8 parts
     small("noalloc_causal_n600_h2", 1, 2, 600, 64, 73, causal=True),  # 4.7 MiB, Pass 1 in 4
 ]
