@@ -14,6 +14,10 @@
 //     with E' = <dO, ddO~> where the split kernel forms alpha by MFMA (d = 64 with the
 //     default row sums), else the sum of the parts' E' (fp32 row sums; d = 128);
 //   Pass 2: dK~ = sum of tau dK~ parts,  dV~ = sum of dV~ parts.
+// When Pass 1's row tiles fill at least one whole round of the CUs, the heads of the
+// whole rounds run unsplit (a launch over that head range) and only the rest split, so
+// that the last, partly idle round is filled while a third (B=1 H=12 N=4096) of the
+// partial sums are written.
 // Every output is still written exactly once, with no atomics.  With the causal mask
 // (d = 64) a Pass 2 work-group sweeps two column tiles, p and n - 1 - p, whose row
 // steps together are the same for every pair; the split cuts that joint sweep into
