@@ -68,9 +68,9 @@ struct Pass2Args {
 // split), and the device workspace the partial sums need.
 struct SplitPlan {
   int s1 = 1, s2 = 1;
-  // Pass 1 with s1 > 1: the first full1 flattened query heads (whole rounds of row
-  // tiles) run unsplit and only the rest split in s1 parts; 0 splits every head.
-  int64_t full1 = 0;
+  // With s1 > 1 (s2 > 1): the first full1 flattened query heads (full2 key/value heads),
+  // whole rounds of work-groups, run unsplit and only the rest split; 0 splits every head.
+  int64_t full1 = 0, full2 = 0;
   int64_t bytes1 = 0, bytes2 = 0;  // Pass 1 / Pass 2 partials (the two reuse one buffer)
   int64_t bytes() const { return bytes1 > bytes2 ? bytes1 : bytes2; }
 };

@@ -14,10 +14,10 @@
 //     with E' = <dO, ddO~> where the split kernel forms alpha by MFMA (d = 64 with the
 //     default row sums), else the sum of the parts' E' (fp32 row sums; d = 128);
 //   Pass 2: dK~ = sum of tau dK~ parts,  dV~ = sum of dV~ parts.
-// When Pass 1's row tiles fill at least one whole round of the CUs, the heads of the
+// When a pass's work-groups fill at least one whole round of the CUs, the heads of the
 // whole rounds run unsplit (a launch over that head range) and only the rest split, so
-// that the last, partly idle round is filled while a third (B=1 H=12 N=4096) of the
-// partial sums are written.
+// that the last, partly idle round is filled while only the rest's partial sums are
+// written (a third of them for Pass 1 at B=1 H=12 N=4096).
 // Every output is still written exactly once, with no atomics.  With the causal mask
 // (d = 64) a Pass 2 work-group sweeps two column tiles, p and n - 1 - p, whose row
 // steps together are the same for every pair; the split cuts that joint sweep into
@@ -117,6 +117,50 @@ int choose_parts(int64_t units, int64_t stages, double sweep_us, double part_byt
 
 }  // namespace
 
+namespace {
+
+// How one pass splits: every head's work-groups in s parts (full = 0), or the first
+// `full` heads, whole rounds of work-groups, unsplit and only the rest in s parts.
+struct PassSplit {
+  int s = 1;
+  int64_t full = 0;
+};
+
+// per_head work-groups (tiles or tile pairs) for each of `heads` heads, each sweeping
+// `stages` stages in sweep_us, with head_bytes of partial sums per head and part;
+// whole(f) tells whether the first f heads form a problem of their own.  Leaving the
+// heads of whole rounds unsplit takes the same rounds of sweep time as splitting every
+// head and writes only the rest's partial sums (B=1 H=12 N=4096, Pass 1: 8 heads whole,
+// 4 in two parts, a third of the partials); it is taken where the estimate is lower.
+template <typename Whole>
+PassSplit plan_pass(int64_t per_head, int64_t heads, int64_t stages, double sweep_us,
+                    double head_bytes, Whole whole) {
+  PassSplit r;
+  const int64_t units = per_head * heads;
+  r.s = choose_parts(units, stages, sweep_us, heads * head_bytes);
+  if (units < kCUs || per_head > kCUs) return r;
+  const int64_t per_round = kCUs / per_head;  // heads per round of work-groups
+  const int64_t full = units / kCUs * per_round;
+  const int64_t rest = heads - full;
+  if (rest <= 0 || !whole(full)) return r;
+  const int s_rest = choose_parts(rest * per_head, stages, sweep_us, rest * head_bytes);
+  if (s_rest == 1) return r;
+  const auto est = [&](int64_t u, int s, double bytes) {
+    const double rounds = (double)((u * s + kCUs - 1) / kCUs);
+    return rounds * sweep_us / s + (s > 1 ? 2.0 * s * bytes / 5.0e6 + 5.0 : 0.0);
+  };
+  const double uniform = est(units, r.s, heads * head_bytes);
+  const double partial =
+      (double)(full / per_round) * sweep_us + est(rest * per_head, s_rest, rest * head_bytes);
+  if (partial < uniform && (r.s > 1 || partial <= 0.95 * est(units, 1, 0.0))) {
+    r.s = s_rest;
+    r.full = full;
+  }
+  return r;
+}
+
+}  // namespace
+
 SplitPlan split_plan(const Problem& p) {
   SplitPlan plan;
   // The split forms exist for the shipped bf16 variants; with the causal mask only at
@@ -132,59 +176,44 @@ SplitPlan split_plan(const Problem& p) {
   // of the group's query heads, or (causal, d = 64) a pair of tiles p and n - 1 - p
   // sweeping the rows from each tile's first key on, 2 n_stages - 4 (n - 1) steps per
   // query head for every pair.
-  int64_t units2 = col_tiles * heads_kv;
+  int64_t per_head2 = col_tiles;
   int64_t steps2 = stages * group;
   if (p.causal) {
-    units2 = (col_tiles + 1) / 2 * heads_kv;
+    per_head2 = (col_tiles + 1) / 2;
     steps2 = (col_tiles > 1 ? 2 * stages - 4 * (col_tiles - 1) : stages) * group;
   }
   // Measured sweep times of one work-group per key (Pass 1) or row step of 64 rows
   // (Pass 2): ~35 and ~74 ns per key, ~3.1 and ~3.7 us per row step at d = 64 / 128.
   const double sweep2 = (p.d == 64 ? 3.1 : 3.7) * steps2;
-  const double part2 = (double)heads_kv * p.N * 2 * p.d * 4;  // bytes of one part
-  plan.s2 = choose_parts(units2, steps2, sweep2, part2);
-  if (plan.s2 > 1) plan.bytes2 = (int64_t)plan.s2 * heads_kv * p.N * 2 * p.d * 4;
+  const double head_bytes2 = (double)p.N * 2 * p.d * 4;  // one key/value head, one part
+  // a leading range of key/value heads is a problem of its own in one batch, or when
+  // it holds whole batches
+  const PassSplit s2 = plan_pass(per_head2, heads_kv, steps2, sweep2, head_bytes2,
+                                 [&](int64_t f) { return p.B == 1 || f % p.Hkv == 0; });
+  plan.s2 = s2.s;
+  plan.full2 = s2.full;
+  if (plan.s2 > 1) plan.bytes2 = (int64_t)plan.s2 * (heads_kv - s2.full) * p.N * 2 * p.d * 4;
   // Pass 1 work-groups and their 64-key stages: one row tile of 128 rows sweeping
   // every key, or (causal, d = 64) row tiles n - 1 - p and p, 2 (n + 1) stages for
   // every pair when N is a multiple of 128 (the keys up to each tile's last row).
   const int64_t row_tiles = (p.N + 127) / 128;
-  int64_t units1 = row_tiles * heads_q;
+  int64_t per_head1 = row_tiles;
   int64_t stages1 = stages;
   if (p.causal) {
-    units1 = (row_tiles + 1) / 2 * heads_q;
+    per_head1 = (row_tiles + 1) / 2;
     stages1 = row_tiles > 1 ? stages + 2 : stages;
   }
   const double sweep1 = (p.d == 64 ? 0.035 : 0.074) * 64 * stages1;
-  const double row_bytes1 = (double)p.N * (4 * p.d + 2) * 4;  // one head's partials, one part
-  plan.s1 = choose_parts(units1, stages1, sweep1, heads_q * row_bytes1);
-  if (plan.s1 > 1) plan.bytes1 = (int64_t)plan.s1 * heads_q * p.N * (4 * p.d + 2) * 4;
-  // Without the mask, when the row tiles fill at least one whole round, the heads of
-  // the whole rounds can run unsplit and only the heads of the last, partly idle round
-  // split (B=1 H=12 N=4096: 8 heads unsplit, 4 in two parts): the same rounds of sweep
-  // time, a third of the partial sums.  The leading heads must be whole groups of
-  // query heads (one batch) or whole batches, so that both parts are problems of
-  // their own.
-  if (!p.causal && units1 >= kCUs && row_tiles <= kCUs) {
-    const int64_t per_round = kCUs / row_tiles;  // heads per round of work-groups
-    const int64_t full = units1 / kCUs * per_round;
-    const int64_t rest = heads_q - full;
-    const bool whole = p.B == 1 ? full % group == 0 : full % p.Hq == 0;
-    if (rest > 0 && whole) {
-      const int s_rest = choose_parts(rest * row_tiles, stages1, sweep1, rest * row_bytes1);
-      const auto est = [&](int64_t units, int s, double bytes) {
-        const double rounds = (double)((units * s + kCUs - 1) / kCUs);
-        return rounds * sweep1 / s + (s > 1 ? 2.0 * s * bytes / 5.0e6 + 5.0 : 0.0);
-      };
-      const double uniform = est(units1, plan.s1, heads_q * row_bytes1);
-      const double partial = (double)(full / per_round) * sweep1 +
-                             est(rest * row_tiles, s_rest, rest * row_bytes1);
-      if (s_rest > 1 && partial < uniform) {
-        plan.s1 = s_rest;
-        plan.full1 = full;
-        plan.bytes1 = (int64_t)s_rest * rest * p.N * (4 * p.d + 2) * 4;
-      }
-    }
-  }
+  const double head_bytes1 = (double)p.N * (4 * p.d + 2) * 4;  // one query head, one part
+  // a leading range of query heads must end on a group of query heads (one batch) or
+  // on a batch boundary
+  const PassSplit s1 = plan_pass(per_head1, heads_q, stages1, sweep1, head_bytes1, [&](int64_t f) {
+    return p.B == 1 ? f % group == 0 : f % p.Hq == 0;
+  });
+  plan.s1 = s1.s;
+  plan.full1 = s1.full;
+  if (plan.s1 > 1)
+    plan.bytes1 = (int64_t)plan.s1 * (heads_q - s1.full) * p.N * (4 * p.d + 2) * 4;
   return plan;
 }
 
@@ -222,6 +251,39 @@ void head_range(const Problem& p, const Pass1Args& a, int64_t h0, int64_t n, Pro
   sa->ddOt = a.ddOt + q;
   sa->alpha = a.alpha + r;
   sa->E = a.E + r;
+}
+
+// The key/value heads [h0, h0 + n) of a problem (any range of one batch, or whole
+// batches) with their query heads, as a problem of their own.
+void kv_head_range(const Problem& p, const Pass2Args& a, int64_t h0, int64_t n, Problem* sp,
+                   Pass2Args* sa) {
+  const int64_t group = p.Hq / p.Hkv;
+  *sp = p;
+  if (p.B == 1) {
+    sp->Hkv = (int)n;
+    sp->Hq = (int)(n * group);
+  } else {
+    sp->B = (int)(n / p.Hkv);
+  }
+  const int64_t es = p.bf16 ? 2 : 4;
+  const int64_t kv = h0 * p.N * p.d, q = h0 * group * p.N * p.d, r = h0 * group * p.N;
+  auto in = [&](const void* x, int64_t off) {
+    return static_cast<const void*>(static_cast<const char*>(x) + off * es);
+  };
+  *sa = a;
+  sa->Q = in(a.Q, q);
+  sa->dO = in(a.dO, q);
+  sa->UQ = in(a.UQ, q);
+  sa->K = in(a.K, kv);
+  sa->V = in(a.V, kv);
+  sa->UK = in(a.UK, kv);
+  sa->UV = in(a.UV, kv);
+  sa->L = a.L + r;
+  sa->D = a.D + r;
+  sa->alpha = a.alpha + r;
+  sa->E = a.E + r;
+  sa->dKt = a.dKt + kv;
+  sa->dVt = a.dVt + kv;
 }
 
 }  // namespace
@@ -267,15 +329,24 @@ hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass
     if (e != hipSuccess) return e;
   }
   if (plan.s2 > 1) {
+    Problem p2 = p;
     Pass2Args a2 = a2_in;
-    const int64_t rows = (int64_t)p.B * p.Hkv * p.N;
+    if (plan.full2 > 0) {  // leading key/value heads unsplit, the rest split below
+      Problem pf;
+      Pass2Args af;
+      kv_head_range(p, a2_in, 0, plan.full2, &pf, &af);
+      const hipError_t e = launch_pass2(pf, af, s);
+      if (e != hipSuccess) return e;
+      kv_head_range(p, a2_in, plan.full2, (int64_t)p.B * p.Hkv - plan.full2, &p2, &a2);
+    }
+    const int64_t rows = (int64_t)p2.B * p2.Hkv * p2.N;
     a2.part = reinterpret_cast<float*>(ws);  // Pass 1's partials are consumed by now
     a2.nsplit = plan.s2;
-    hipError_t e = launch_pass2_split(p, a2, s);
+    hipError_t e = launch_pass2_split(p2, a2, s);
     if (e != hipSuccess) return e;
-    const int64_t threads = rows * (p.d / 4);
+    const int64_t threads = rows * (p2.d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
-    if (p.d == 64)
+    if (p2.d == 64)
       hipLaunchKernelGGL(reduce_pass2_kernel<64>, grid, dim3(256), 0, s, a2, rows, plan.s2);
     else
       hipLaunchKernelGGL(reduce_pass2_kernel<128>, grid, dim3(256), 0, s, a2, rows, plan.s2);

@@ -175,8 +175,8 @@ int fbob_bob_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64
  * work-groups that write fp32 partial sums to the workspace, and a reduction kernel
  * adds them in a fixed order (results are deterministic; they differ from
  * fbob_bob's only by the order of the fp32 additions) and writes every output once.
- * When Pass 1's row tiles fill at least one whole round of the CUs, the query heads of
- * the whole rounds run unsplit and only the remaining heads split (if the boundary falls
+ * When a pass's work-groups fill at least one whole round of the CUs, the heads of the
+ * whole rounds run unsplit and only the remaining heads split (where the boundary falls
  * between groups of query heads of one batch, or between batches).
  * Splitting applies to bf16 inputs, d = 64 with tau a power of two or d = 128; with
  * causal != 0 only at d = 64, where a work-group of either pass owns two tiles (p and

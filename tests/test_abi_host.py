@@ -211,8 +211,9 @@ def test_workspace_size_follows_the_split_plan(lib):
     assert ws_size(lib, causal=1) == (OK, 2 * heads * N * 2 * d * 4)
     assert ws_size(lib, causal=1, B=4) == (OK, 0)      # partials would cost more
     assert ws_size(lib, causal=1, d=128, tau=0.125) == (OK, 0)
-    # B=1 H=12 N=16384: 384 tile pairs, 1.5 rounds; two parts fill three whole rounds
-    assert ws_size(lib, causal=1, N=16384) == (OK, 2 * heads * 16384 * 2 * d * 4)
+    # B=1 H=12 N=16384: 384 Pass 2 tile pairs, 1.5 rounds; the first 8 heads fill one
+    # round unsplit, the last 4 split in two parts fill the second
+    assert ws_size(lib, causal=1, N=16384) == (OK, 2 * 4 * 16384 * 2 * d * 4)
     assert ws_size(lib, causal=1, N=16384, B=4) == (OK, 0)
     # B=1 H=4 N=4096: 64 Pass 1 work-groups (16 row-tile pairs x 4 heads) and 32 Pass 2
     # work-groups for 256 CUs: Pass 1 in four parts, Pass 2 in eight; the workspace
@@ -307,11 +308,12 @@ def call_bob_noalloc(lib, B=1, Hq=12, Hkv=12, N=4096, d=64, ptrs=None):
 
 def test_bob_noalloc_validates_before_any_hip_call(lib):
     """Errors that need no GPU: sizes, pointers, and a split schedule larger than the
-    static scratch (B=1 H=10 N=4096 d=128: Pass 2 in four parts of 10 x 4096 rows x
-    2 x 128 fp32, 160 MiB > 128 MiB)."""
-    st, need = ws_size(lib, Hq=10, Hkv=10, N=4096, d=128, tau=1 / 128 ** 0.5)
-    assert st == OK and need == 4 * 10 * 4096 * 2 * 128 * 4 > SCRATCH_BYTES
-    assert call_bob_noalloc(lib, Hq=10, Hkv=10, d=128) == SCRATCH
+    static scratch (B=2 H=10 N=4096 d=128: the heads of Pass 2's whole round would end
+    inside a batch, so every head splits in two parts of 20 x 4096 rows x 2 x 128 fp32,
+    160 MiB > 128 MiB)."""
+    st, need = ws_size(lib, B=2, Hq=10, Hkv=10, N=4096, d=128, tau=1 / 128 ** 0.5)
+    assert st == OK and need == 2 * 20 * 4096 * 2 * 128 * 4 > SCRATCH_BYTES
+    assert call_bob_noalloc(lib, B=2, Hq=10, Hkv=10, d=128) == SCRATCH
     # the C2 problem fits (its workspace is 32.25 MiB), and so does its d = 128 form
     assert 0 < ws_size(lib)[1] <= SCRATCH_BYTES
     assert 0 < ws_size(lib, d=128, tau=1 / 128 ** 0.5)[1] <= SCRATCH_BYTES
@@ -320,7 +322,7 @@ def test_bob_noalloc_validates_before_any_hip_call(lib):
     fb = FakeBuffers(16)
     ptrs = [fb[m] for m in range(16)]
     ptrs[3] = ctypes.c_void_p(0)
-    assert call_bob_noalloc(lib, Hq=10, Hkv=10, d=128, ptrs=ptrs) == INVALID  # before scratch
+    assert call_bob_noalloc(lib, B=2, Hq=10, Hkv=10, d=128, ptrs=ptrs) == INVALID  # first
     ptrs = [fb[m] for m in range(16)]
     ptrs[10] = ctypes.c_void_p(fb.addrs[0])                         # dQ~ on top of Q
-    assert call_bob_noalloc(lib, Hq=10, Hkv=10, d=128, ptrs=ptrs) == ALIAS
+    assert call_bob_noalloc(lib, B=2, Hq=10, Hkv=10, d=128, ptrs=ptrs) == ALIAS

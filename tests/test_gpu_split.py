@@ -3,8 +3,9 @@
 With a workspace, problems too small to fill the GPU split each Pass 1 row tile's
 key sweep and each Pass 2 column tile's row sweep over several work-groups, which
 write fp32 partial sums that a reduction kernel adds.  Where Pass 1's row tiles fill
-whole rounds of the CUs and leave a partial one, the heads of the whole rounds run
-unsplit and only the rest split (a launch on each head range).  With the causal mask (d = 64)
+whole rounds of the CUs and leave a partial one (either pass, with or without the mask),
+the heads of the whole rounds run unsplit and only the rest split (a launch on each head
+range).  With the causal mask (d = 64)
 a work-group sweeps two tiles (row tiles n - 1 - p and p in Pass 1, column tiles p and
 n - 1 - p in Pass 2), and the split cuts that joint sweep, so a part can end in one
 tile and begin the other.  The outputs are checked against the fp64 oracle (same bars as the unsplit
@@ -110,6 +111,37 @@ def test_causal_split_at_the_gpt2_heads_shape():
     ora = U.oracle_full(inp, w, heads=[(0, 0), (0, w.H - 1)])
     errs = U.compare_full(gpu, ora, w, keys=U.ALL_KEYS)
     U.say(f"[split] {w.name} vs oracle (2 heads): " +
+          " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+
+
+# Pass 2, and the causal pairs of both passes, with the heads of whole rounds unsplit
+# and the rest split: 40 heads at N = 2048 (Pass 1: 32 heads whole and 8 in two parts;
+# Pass 2: 32 whole and 8 in four), the causal mask at N = 4096 (pairs of tiles: Pass 1
+# 32 + 8 in two, Pass 2 32 + 8 in four) and 40 key/value heads shared by 80 query heads
+# (Pass 2 over key/value head ranges: 32 whole, 8 in four).  The first and the last
+# group of heads (one from each part) against the oracle, every head against the
+# unsplit call.
+PARTIAL = [
+    case("split_partial_h40_n2048", 1, 40, 2048, 64, "bf16", 77),
+    case("split_partial_causal_h40_n4096", 1, 40, 4096, 64, "bf16", 78, causal=True),
+    case("split_partial_gqa_hq80_hkv40_n2048", 1, 80, 2048, 64, "bf16", 79, Hkv=40),
+]
+
+
+@pytest.mark.parametrize("w", PARTIAL, ids=[w.name for w in PARTIAL])
+def test_partial_split_first_and_last_heads_against_oracle(w):
+    U.say(f"[split] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    inp = U.make_inputs(w)
+    dev = U.to_device(inp, w.dtype)
+    need, out, ref, _ = run_ws(dev, w)
+    assert need > 0, "the case is meant to take the split schedule"
+    check_against_unsplit(w, out, ref)
+    group = w.H // w.extra.get("Hkv", w.H)
+    heads = [(0, h) for h in list(range(group)) + list(range(w.H - group, w.H))]
+    gpu = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+    errs = U.compare_full(gpu, U.oracle_full(inp, w, heads=heads), w, keys=U.ALL_KEYS)
+    U.say(f"[split] {w.name} vs oracle (first and last groups): " +
           " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
 
