@@ -31,6 +31,7 @@ PROTOTYPES = {
     "fbob_bob_noalloc": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp]),
     "fbob_bob_ex": (_i, _SIZES + [_i] + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp, _i64] + [_vp]),
     "fbob_strerror": (ctypes.c_char_p, [_i]),
+    "fbob_hip_error_string": (ctypes.c_char_p, []),
     "fbob_version": (_i, []),
 }
 
@@ -40,7 +41,10 @@ class FbobError(RuntimeError):
         self.status = status
         msg = STATUS.get(status, f"status {status}")
         try:
-            msg += ": " + load_library().fbob_strerror(status).decode()
+            lib = load_library()
+            msg += ": " + lib.fbob_strerror(status).decode()
+            if status == 5:  # FBOB_ERR_HIP: name the HIP error behind it
+                msg += f" ({lib.fbob_hip_error_string().decode()})"
         except Exception:  # pragma: no cover - message only
             pass
         super().__init__(msg)
@@ -74,6 +78,11 @@ def load_library(path: str | None = None):
         raise RuntimeError(
             f"{p} is missing: build the HIP library first "
             "(python -m exact_softmax_attention_fbob_amd.build)")
+    # torch first: its HIP runtime (libamdhip64.so.7, which torch loads by another file
+    # name) must be in the process before the library asks for libamdhip64.so.7, so that
+    # the dynamic loader hands the library that same runtime.  Loaded the other way round,
+    # the process would hold two HIP runtimes and the library's would find no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     for name, (res, argt) in PROTOTYPES.items():
         fn = getattr(lib, name)

@@ -86,7 +86,19 @@ int check_ptrs(const void* const* ins, const int64_t* in_bytes, int n_in, void* 
   return FBOB_OK;
 }
 
-int finish(hipError_t e) { return e == hipSuccess ? FBOB_OK : FBOB_ERR_HIP; }
+// HIP error behind the calling thread's last FBOB_ERR_HIP (fbob_hip_error_string).
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int finish(hipError_t e) {
+  if (e == hipSuccess) return FBOB_OK;
+  g_last_hip_error = e;
+  return FBOB_ERR_HIP;
+}
+
+// Called after validation, right before an entry point's launches: takes any error
+// still pending on the calling thread from earlier HIP calls (the caller's or another
+// library's), so that the hipGetLastError after each launch reports that launch only.
+void clear_pending() { (void)hipGetLastError(); }
 
 // Pointer checks shared by the BoB entry points: the ten inputs, the six outputs
 // and, when it will be used, the workspace of ws_bytes as a seventh output.
@@ -108,8 +120,10 @@ int check_bob_ptrs(const Checked& c, int64_t B, int64_t Hq, int64_t Hkv, int64_t
 // Both passes on one stream, split when a workspace is given.
 int run_bob(const Checked& c, const fbob::SplitPlan& plan, fbob::Pass1Args a1,
             fbob::Pass2Args a2, void* workspace, hipStream_t s) {
+  clear_pending();
   if (workspace != nullptr) return finish(fbob::launch_bob_split(c.p, a1, a2, plan, workspace, s));
-  if (fbob::launch_pass1(c.p, a1, s) != hipSuccess) return FBOB_ERR_HIP;
+  const int st = finish(fbob::launch_pass1(c.p, a1, s));
+  if (st != FBOB_OK) return st;
   return finish(fbob::launch_pass2(c.p, a2, s));
 }
 
@@ -121,18 +135,19 @@ void* g_scratch_address[kMaxDevices] = {};
 // looked up with hipGetSymbolAddress on the first call on each device, then cached.
 int scratch_address(hipStream_t s, void** out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return FBOB_ERR_HIP;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return finish(e);
   if (s != nullptr) {
     hipDevice_t sdev = -1;
-    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return FBOB_ERR_HIP;
+    if (const hipError_t e = hipStreamGetDevice(s, &sdev); e != hipSuccess) return finish(e);
     if (sdev != dev) return FBOB_ERR_INVALID_ARG;
   }
   if (dev < 0 || dev >= kMaxDevices) return FBOB_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (g_scratch_address[dev] == nullptr) {
     void* addr = nullptr;
-    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
-      return FBOB_ERR_HIP;
+    if (const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)); e != hipSuccess)
+      return finish(e);
+    if (addr == nullptr) return FBOB_ERR_HIP;
     g_scratch_address[dev] = addr;
   }
   *out = g_scratch_address[dev];
@@ -144,6 +159,10 @@ int scratch_address(hipStream_t s, void** out) {
 extern "C" {
 
 int fbob_version(void) { return FBOB_VERSION; }
+
+const char* fbob_hip_error_string(void) {
+  return g_last_hip_error == hipSuccess ? "no HIP error" : hipGetErrorName(g_last_hip_error);
+}
 
 const char* fbob_strerror(int status) {
   switch (status) {
@@ -177,6 +196,7 @@ int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64
   const int st = check_ptrs(ins, inb, with_d ? 4 : 3, outs, outb, with_d ? 3 : 2);
   if (st != FBOB_OK) return st;
   fbob::FwdArgs a{Q, K, V, dO, O, L, D};
+  clear_pending();
   return finish(fbob::launch_forward(c.p, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -197,6 +217,7 @@ int fbob_bob_pass1(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
   const int st = check_ptrs(ins, inb, 10, outs, outb, 4);
   if (st != FBOB_OK) return st;
   fbob::Pass1Args a{Q, K, V, dO, UQ, UK, UV, O, L, D, dQt, ddOt, alpha, E};
+  clear_pending();
   return finish(fbob::launch_pass1(c.p, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -217,6 +238,7 @@ int fbob_bob_pass2(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
   const int st = check_ptrs(ins, inb, 11, outs, outb, 2);
   if (st != FBOB_OK) return st;
   fbob::Pass2Args a{Q, K, V, dO, UQ, UK, UV, L, D, alpha, E, dKt, dVt};
+  clear_pending();
   return finish(fbob::launch_pass2(c.p, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -238,7 +260,9 @@ int fbob_backward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
   if (st != FBOB_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   fbob::GradArgs a{Q, K, V, dO, O, L, dQ, dK, dV, D};
-  if (fbob::launch_grad_dq(c.p, a, s) != hipSuccess) return FBOB_ERR_HIP;
+  clear_pending();
+  const int st1 = finish(fbob::launch_grad_dq(c.p, a, s));
+  if (st1 != FBOB_OK) return st1;
   return finish(fbob::launch_grad_dkv(c.p, a, s));
 }
 

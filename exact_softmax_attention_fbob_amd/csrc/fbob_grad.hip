@@ -442,6 +442,9 @@ hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s) {
 #if FBOB_TUNING
       if (cfg == 1) return launch_dq<__bf16, 64, 8, 64, true, 1>(p, a, s);
       if (cfg == 2) return launch_dq<__bf16, 64, 8, 64, true, 2>(p, a, s);
+      // four-wave work-groups: three per CU at 64-key stages, two at 128
+      if (cfg == 3) return launch_dq<__bf16, 64, 4, 64, true, 2>(p, a, s);
+      if (cfg == 4) return launch_dq<__bf16, 64, 4, 128, true, 2>(p, a, s);
 #endif
       return launch_dq<__bf16, 64, 8, 128, true, 2>(p, a, s);
     }
@@ -457,6 +460,11 @@ hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s) {
 
 hipError_t launch_grad_dkv(const Problem& p, const GradArgs& a, hipStream_t s) {
   if (p.bf16) {
+#if FBOB_TUNING
+    // four-wave work-groups (two or three per CU, by registers)
+    if (p.d == 64 && tune_choice("FBOB_TUNE_DKV") == 1)
+      return launch_dkv<__bf16, 64, 4, 2, 64, true>(p, a, s);
+#endif
     if (p.d == 64) return launch_dkv<__bf16, 64, 8, 2, 64, true>(p, a, s);
     return launch_dkv<__bf16, 128, 8, 1, 32, true>(p, a, s);
   }

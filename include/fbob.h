@@ -41,7 +41,10 @@
  *                            per-head indexing
  *      FBOB_ERR_ALIGNMENT    a pointer not 16-byte aligned
  *      FBOB_ERR_ALIAS        an output range overlaps an input or another output
- *      FBOB_ERR_HIP          a HIP launch error (hipGetLastError after launch)
+ *      FBOB_ERR_HIP          a HIP launch error (hipGetLastError after launch; an
+ *                            error the calling thread left pending before the call is
+ *                            taken first and never reported; fbob_hip_error_string
+ *                            names the HIP error)
  *      FBOB_ERR_SCRATCH      fbob_bob_noalloc only: the problem's split schedule
  *                            needs more than FBOB_SCRATCH_BYTES
  */
@@ -256,6 +259,13 @@ int fbob_bob_ex(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_
                 float* dQt, float* dKt, float* dVt, float* ddOt,
                 float* alpha, float* E, void* workspace, int64_t workspace_bytes,
                 void* stream);
+
+/*
+ * Name of the HIP error behind the calling thread's last FBOB_ERR_HIP (a static string,
+ * e.g. "hipErrorInvalidConfiguration"), or "no HIP error" if that thread has had none.
+ * Thread-local; no GPU call.
+ */
+const char* fbob_hip_error_string(void);
 
 /* Static string naming a status code ("unknown status" for other values). */
 const char* fbob_strerror(int status);

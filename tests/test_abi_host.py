@@ -38,7 +38,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["fbob_forward", "fbob_backward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
          "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_bob_ex", "fbob_bob_noalloc",
-         "fbob_strerror", "fbob_version"])
+         "fbob_strerror", "fbob_hip_error_string", "fbob_version"])
     assert sorted(_lib.PROTOTYPES) == declared_functions()
 
 
@@ -49,6 +49,8 @@ def test_library_exports_every_declared_symbol(lib):
     for st in range(7):
         assert lib.fbob_strerror(st) != b"unknown status"
     assert lib.fbob_strerror(99) == b"unknown status"
+    # no launch has failed on this thread (validation errors are not HIP errors)
+    assert lib.fbob_hip_error_string() == b"no HIP error"
 
 
 class FakeBuffers:

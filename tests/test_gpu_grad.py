@@ -98,13 +98,15 @@ def test_backward_small_cases_full_oracle(w):
     assert all(v <= tol for v in errs.values()), errs
 
 
-DQ_VARIANTS = [("FBOB_TUNE_DQ", v) for v in (1, 2)] + [("FBOB_TUNE_DQ_D128", v) for v in (1, 2)]
+DQ_VARIANTS = [("FBOB_TUNE_DQ", v) for v in (1, 2, 3, 4)] + \
+    [("FBOB_TUNE_DQ_D128", v) for v in (1, 2)] + [("FBOB_TUNE_DKV", 1)]
 
 
 @pytest.mark.parametrize("var,val", DQ_VARIANTS, ids=[f"{a}={b}" for a, b in DQ_VARIANTS])
 def test_backward_row_pass_variants(var, val, monkeypatch, tuning_library):
-    """Every compiled layout of the row pass (rows per wave, stage size) against the
-    oracle, on a ragged tail and on a causal grouped-query case."""
+    """Every compiled layout of the row pass (rows per wave, stage size, four-wave
+    work-groups) and the column pass's four-wave layout against the oracle, on a ragged
+    tail and on a causal grouped-query case."""
     d = 128 if var.endswith("D128") else 64
     monkeypatch.setenv(var, str(val))
     for w in (case(f"dqv_n300_b2_h2_d{d}", 2, 2, 300, d, "bf16", 81),
