@@ -552,7 +552,7 @@ def graph_timed(fn, reps):
 
 
 def causal_split(args):
-    """The split schedule on causal problems (d = 64, bf16): fbob_bob against fbob_bob_ws
+    """The split schedule on causal problems (d = 64 and 128, bf16): fbob_bob against fbob_bob_ws
     with the workspace the planner asks for, each timed as a HIP graph of back-to-back
     calls, interleaved over three rounds (median).  Small causal problems leave most CUs
     idle: one work-group per pair of tiles.  One JSON line per shape; the non-causal
@@ -563,19 +563,22 @@ def causal_split(args):
     import exact_softmax_attention_fbob_amd as fb
     import workloads
     base = workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"]
-    shapes = ((1, 12, 4096, True), (1, 12, 4096, False), (1, 4, 4096, True),
-              (1, 12, 2048, True), (1, 12, 1024, True), (1, 12, 16384, True),
-              (2, 12, 8192, True), (4, 12, 4096, True), (8, 12, 1024, True))
-    for (B, H, N, causal) in shapes:
-        w = base.with_(B=B, H=H, N=N, causal=causal, name=f"b{B}_h{H}_n{N}")
-        print(f"[causal-split] B={B} H={H} N={N} causal={causal}", file=sys.stderr, flush=True)
+    shapes = ((1, 12, 4096, True, 64), (1, 12, 4096, False, 64), (1, 4, 4096, True, 64),
+              (1, 12, 2048, True, 64), (1, 12, 1024, True, 64), (1, 12, 16384, True, 64),
+              (2, 12, 8192, True, 64), (4, 12, 4096, True, 64), (8, 12, 1024, True, 64),
+              (1, 12, 4096, True, 128), (1, 4, 4096, True, 128), (1, 2, 8192, True, 128))
+    for (B, H, N, causal, d) in shapes:
+        w = base.with_(B=B, H=H, N=N, d=d, causal=causal, name=f"b{B}_h{H}_n{N}_d{d}",
+                       extra={"tau": 1.0 / d ** 0.5})
+        print(f"[causal-split] B={B} H={H} N={N} d={d} causal={causal}", file=sys.stderr,
+              flush=True)
         T = {k: torch.from_numpy(v).cuda().to(torch.bfloat16)
              for k, v in workloads.make_inputs(w).items()}
         a7 = tuple(T[k] for k in workloads.TENSORS)
         O, L, D = fb.forward(*a7[:4], w.tau, causal)
         need = fb.bob_workspace_size(a7[0], a7[1], w.tau, causal)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-        reps = max(4, min(50, int(4e5 * 12 * 4096 / (B * H * N * N))))
+        reps = max(4, min(50, int(4e5 * 12 * 4096 * 64 / (B * H * N * N * d))))
         unsplit = graph_timed(lambda: fb.bob(*a7, O, L, D, w.tau, causal), reps)
         split = graph_timed(lambda: fb.bob_ws(*a7, O, L, D, w.tau, causal, workspace=ws), reps)
         tu, ts = [], []

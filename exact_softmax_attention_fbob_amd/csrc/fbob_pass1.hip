@@ -509,9 +509,7 @@ hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
   const int n_row_tiles = (p.N + kBR - 1) / kBR;
   const int n_units = p.causal && D < 128 ? (n_row_tiles + 1) / 2 : n_row_tiles;
   const int total = n_units * p.B * p.Hq * a.nsplit;
-  if constexpr (D >= 128) {
-    if (p.causal) return hipErrorInvalidValue;  // split_plan masks only at d = 64
-  } else if (p.causal) {
+  if (p.causal) {
     hipLaunchKernelGGL((pass1_kernel<T, D, NW, NI, SCHED, TM, BC, DIRECT, true, VSUM, true>),
                        dim3(total), dim3(NW * 64), 0, s, a, p.Hq, p.Hq / p.Hkv, p.N, p.tau,
                        n_row_tiles, total);
@@ -526,8 +524,8 @@ hipError_t launch_split_t(const Problem& p, const Pass1Args& a, hipStream_t s) {
 }  // namespace
 
 // The shipped bf16 variants of launch_pass1 below (d = 64 with tau a power of two, with
-// or without the causal mask and with either row-sum form; d = 128 without the mask),
-// in split form; split_plan admits no other problem.
+// either row-sum form; d = 128), with or without the causal mask, in split form;
+// split_plan admits no other problem.
 hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t s) {
   if (p.d == 64 && p.fp32_row_sums)
     return launch_split_t<__bf16, 64, 8, 1, 3, kTauPow2, 64, true, true>(p, a, s);

@@ -362,9 +362,7 @@ hipError_t launch_split_t(const Problem& p, const Pass2Args& a, hipStream_t s) {
   const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
   const int n_units = p.causal && D < 128 ? (n_col_tiles + 1) / 2 : n_col_tiles;
   const int total = n_units * p.B * p.Hkv * a.nsplit;
-  if constexpr (D >= 128) {
-    if (p.causal) return hipErrorInvalidValue;  // split_plan masks only at d = 64
-  } else if (p.causal) {
+  if (p.causal) {
     hipLaunchKernelGGL((pass2_kernel<T, D, NW, NJ, BRS, SCHED, TM, DIRECT, true, true>),
                        dim3(total), dim3(NW * 64), 0, s, a, p.Hkv, p.Hq / p.Hkv, p.N, p.tau,
                        n_col_tiles, total);

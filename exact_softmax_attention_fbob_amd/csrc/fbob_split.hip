@@ -19,10 +19,12 @@
 // that the last, partly idle round is filled while only the rest's partial sums are
 // written (a third of them for Pass 1 at B=1 H=12 N=4096).
 // Every output is still written exactly once, with no atomics.  With the causal mask
-// (d = 64) a Pass 2 work-group sweeps two column tiles, p and n - 1 - p, whose row
-// steps together are the same for every pair; the split cuts that joint sweep into
-// equal parts; causal Pass 1 pairs its row tiles n - 1 - p and p, and splits the
-// same way.
+// at d = 64 a Pass 2 work-group sweeps two column tiles, p and n - 1 - p, whose row
+// steps together are the same for every pair, and causal Pass 1 pairs its row tiles
+// n - 1 - p and p; the split cuts each pair's joint sweep into equal parts.  At d = 128
+// the tiles are single (longest first) and each tile's own sweep is cut.
+#include <algorithm>
+
 #include "fbob_device.hpp"
 #include "fbob_launch.hpp"
 
@@ -163,10 +165,11 @@ PassSplit plan_pass(int64_t per_head, int64_t heads, int64_t stages, double swee
 
 SplitPlan split_plan(const Problem& p) {
   SplitPlan plan;
-  // The split forms exist for the shipped bf16 variants; with the causal mask only at
-  // d = 64, where the tiles of both passes are paired.
+  // The split forms exist for the shipped bf16 variants.  With the causal mask the tiles
+  // of both passes are paired at d = 64 (every pair the same work) and single at d = 128,
+  // where the tiles' lengths vary; there the model takes the mean tile.
   if (!p.bf16 || (p.d == 64 && !tau_is_pow2(p.tau))) return plan;
-  if (p.causal && p.d != 64) return plan;
+  const bool fold = p.causal && p.d == 64;
   const int64_t heads_q = (int64_t)p.B * p.Hq, heads_kv = (int64_t)p.B * p.Hkv;
   const int64_t group = p.Hq / p.Hkv;
   const int64_t stages = (p.N + 63) / 64;  // 64-key / 64-row stages in both passes
@@ -178,9 +181,11 @@ SplitPlan split_plan(const Problem& p) {
   // query head for every pair.
   int64_t per_head2 = col_tiles;
   int64_t steps2 = stages * group;
-  if (p.causal) {
+  if (fold) {
     per_head2 = (col_tiles + 1) / 2;
     steps2 = (col_tiles > 1 ? 2 * stages - 4 * (col_tiles - 1) : stages) * group;
+  } else if (p.causal) {  // tile c sweeps the rows from its first key on
+    steps2 = std::max<int64_t>(1, (stages + 1) / 2) * group;
   }
   // Measured sweep times of one work-group per key (Pass 1) or row step of 64 rows
   // (Pass 2): ~35 and ~74 ns per key, ~3.1 and ~3.7 us per row step at d = 64 / 128.
@@ -188,8 +193,14 @@ SplitPlan split_plan(const Problem& p) {
   const double head_bytes2 = (double)p.N * 2 * p.d * 4;  // one key/value head, one part
   // a leading range of key/value heads is a problem of its own in one batch, or when
   // it holds whole batches
-  const PassSplit s2 = plan_pass(per_head2, heads_kv, steps2, sweep2, head_bytes2,
-                                 [&](int64_t f) { return p.B == 1 || f % p.Hkv == 0; });
+  // Single causal tiles (d = 128) of unequal length already balance over the CUs when
+  // dispatched longest first; they split only while they do not fill one round
+  // (B=1 H=12 N=4096 split anyway measured 36 % slower, H=4 1.75x faster).
+  const bool single = p.causal && !fold;
+  PassSplit s2;
+  if (!single || per_head2 * heads_kv < kCUs)
+    s2 = plan_pass(per_head2, heads_kv, steps2, sweep2, head_bytes2,
+                   [&](int64_t f) { return p.B == 1 || f % p.Hkv == 0; });
   plan.s2 = s2.s;
   plan.full2 = s2.full;
   if (plan.s2 > 1) plan.bytes2 = (int64_t)plan.s2 * (heads_kv - s2.full) * p.N * 2 * p.d * 4;
@@ -199,17 +210,21 @@ SplitPlan split_plan(const Problem& p) {
   const int64_t row_tiles = (p.N + 127) / 128;
   int64_t per_head1 = row_tiles;
   int64_t stages1 = stages;
-  if (p.causal) {
+  if (fold) {
     per_head1 = (row_tiles + 1) / 2;
     stages1 = row_tiles > 1 ? stages + 2 : stages;
+  } else if (p.causal) {  // tile r sweeps the keys up to its last row
+    stages1 = std::max<int64_t>(1, (stages + 1) / 2);
   }
   const double sweep1 = (p.d == 64 ? 0.035 : 0.074) * 64 * stages1;
   const double head_bytes1 = (double)p.N * (4 * p.d + 2) * 4;  // one query head, one part
   // a leading range of query heads must end on a group of query heads (one batch) or
   // on a batch boundary
-  const PassSplit s1 = plan_pass(per_head1, heads_q, stages1, sweep1, head_bytes1, [&](int64_t f) {
-    return p.B == 1 ? f % group == 0 : f % p.Hq == 0;
-  });
+  PassSplit s1;
+  if (!single || per_head1 * heads_q < kCUs)
+    s1 = plan_pass(per_head1, heads_q, stages1, sweep1, head_bytes1, [&](int64_t f) {
+      return p.B == 1 ? f % group == 0 : f % p.Hq == 0;
+    });
   plan.s1 = s1.s;
   plan.full1 = s1.full;
   if (plan.s1 > 1)

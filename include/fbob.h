@@ -181,10 +181,10 @@ int fbob_bob_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64
  * When a pass's work-groups fill at least one whole round of the CUs, the heads of the
  * whole rounds run unsplit and only the remaining heads split (where the boundary falls
  * between groups of query heads of one batch, or between batches).
- * Splitting applies to bf16 inputs, d = 64 with tau a power of two or d = 128; with
- * causal != 0 only at d = 64, where a work-group of either pass owns two tiles (p and
- * n - 1 - p, so that every work-group has the same masked work) and the split cuts
- * the two tiles' joint sweep into equal parts.
+ * Splitting applies to bf16 inputs, d = 64 with tau a power of two or d = 128.  With
+ * causal != 0 at d = 64 a work-group of either pass owns two tiles (p and n - 1 - p,
+ * so that every work-group has the same masked work) and the split cuts the two
+ * tiles' joint sweep into equal parts; at d = 128 each tile's own sweep is cut.
  *   workspace       DEVICE pointer, 16-byte aligned, owned by the caller, at least
  *                   fbob_bob_workspace_size() bytes; NULL (or fewer bytes) runs the
  *                   unsplit schedule, i.e. exactly fbob_bob.  Its contents on entry

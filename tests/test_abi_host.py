@@ -199,8 +199,8 @@ def test_workspace_size_follows_the_split_plan(lib):
     parts were measured slower there: the partial sums cost more than the idle quarter
     of the CUs), so the workspace holds the 4 heads' Pass 1 partials alone.  With the
     causal mask only Pass 2 splits, at d = 64: the same shape has 96 work-groups of
-    paired column tiles there, split in two.  Problems that fill the GPU, causal
-    d = 128, fp32 and a tau that is not a power of two at d = 64 need none."""
+    paired column tiles there, split in two.  Problems that fill the GPU, fp32 and a
+    tau that is not a power of two at d = 64 need none."""
     heads, N, d = 12, 4096, 64
     assert ws_size(lib) == (OK, 2 * 4 * N * (4 * d + 2) * 4)
     # whole batches unsplit (B=3 H=4: batches 0-1, 256 tiles), the last one in two parts
@@ -212,7 +212,12 @@ def test_workspace_size_follows_the_split_plan(lib):
     assert ws_size(lib, N=16384) == (OK, 0)            # 1536 and 768 tiles: whole rounds
     assert ws_size(lib, causal=1) == (OK, 2 * heads * N * 2 * d * 4)
     assert ws_size(lib, causal=1, B=4) == (OK, 0)      # partials would cost more
+    # causal at d = 128: single tiles, split (each tile's own sweep) only while a pass's
+    # tiles do not fill one round: H=12 N=4096 (384 tiles each pass) stays whole, H=4
+    # (128 tiles) splits
     assert ws_size(lib, causal=1, d=128, tau=0.125) == (OK, 0)
+    st, b = ws_size(lib, causal=1, d=128, tau=0.125, Hq=4, Hkv=4)
+    assert st == OK and b > 0
     # B=1 H=12 N=16384: 384 Pass 2 tile pairs, 1.5 rounds; the first 8 heads fill one
     # round unsplit, the last 4 split in two parts fill the second
     assert ws_size(lib, causal=1, N=16384) == (OK, 2 * 4 * 16384 * 2 * d * 4)

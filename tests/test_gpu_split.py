@@ -45,6 +45,11 @@ SPLIT_CASES = [
     case("split_causal_gqa_hq8_hkv2_n700", 1, 8, 700, 64, "bf16", 67, Hkv=2, causal=True),
     case("split_causal_n2048_b2_h3_qk2", 2, 3, 2048, 64, "bf16", 68, causal=True,
          scale_qk=2.0),                                           # Pass 1 in 4, Pass 2 in 8
+    # causal at d = 128: single tiles (longest first), each tile's own sweep cut, so the
+    # first tiles' parts are short or empty; ragged, and grouped heads
+    case("split_causal_d128_n1000_h2", 1, 2, 1000, 128, "bf16", 80, causal=True),
+    case("split_causal_d128_gqa_hq6_hkv2_n600", 1, 6, 600, 128, "bf16", 81, Hkv=2,
+         causal=True),
     # Pass 1 unsplit on the heads of whole rounds, split on the rest (384 row tiles: 256
     # in one round unsplit, 128 in two parts): grouped heads (the unsplit part ends on a
     # group boundary, the split part starts at K/V head 8), whole batches (batches 0-1
