@@ -646,6 +646,59 @@ def n_sweep(args):
         torch.cuda.empty_cache()
 
 
+def split_audit(args):
+    """Check of the split planner: fbob_bob against fbob_bob_ws (the workspace the
+    planner asks for) on a grid of small and medium shapes (d = 64 and 128, with and
+    without the mask, 1-20 heads, grouped heads, B up to 3, N 2048-32768), each timed
+    as a HIP graph of back-to-back calls, interleaved over three rounds (median).  One
+    JSON line per shape; "slower" marks a split that lost more than 2 %."""
+    import json as _json
+    import statistics
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    import workloads
+    base = workloads.WORKLOADS["gpt2_heads_h12_n4096_d64_bf16"]
+    grid = ((1, 2, 2, 4096), (1, 6, 6, 4096), (1, 12, 12, 4096), (1, 20, 20, 4096),
+            (2, 12, 12, 4096), (1, 12, 4, 4096), (1, 12, 12, 8192), (1, 4, 4, 16384),
+            (1, 1, 1, 32768), (1, 2, 2, 2048), (3, 4, 4, 2048))
+    slower = 0
+    for d in (64, 128):
+        for causal in (False, True):
+            for (B, H, Hkv, N) in grid:
+                w = base.with_(B=B, H=H, N=N, d=d, causal=causal,
+                               name=f"b{B}_h{H}_hkv{Hkv}_n{N}_d{d}",
+                               extra={"tau": 1.0 / d ** 0.5, "Hkv": Hkv})
+                print(f"[split-audit] {w.name} causal={causal}", file=sys.stderr, flush=True)
+                T = workloads.make_inputs_device(w)
+                for k in ("K", "V", "UK", "UV"):
+                    T[k] = T[k][:, :Hkv].contiguous()
+                a7 = tuple(T[k] for k in workloads.TENSORS)
+                O, L, D = fb.forward(*a7[:4], w.tau, causal)
+                need = fb.bob_workspace_size(a7[0], a7[1], w.tau, causal)
+                out = {"B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
+                       "workspace_bytes": need}
+                if need > 0:
+                    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+                    pairs = N * (N + 1) / 2 if causal else N * N
+                    reps = max(3, min(40, int(40 * 12 * 4096 ** 2 * 64 / (B * H * pairs * d))))
+                    unsplit = graph_timed(lambda: fb.bob(*a7, O, L, D, w.tau, causal), reps)
+                    split = graph_timed(lambda: fb.bob_ws(*a7, O, L, D, w.tau, causal,
+                                                          workspace=ws), reps)
+                    tu, ts = [], []
+                    for _ in range(3):
+                        tu.append(unsplit())
+                        ts.append(split())
+                    u, sp = statistics.median(tu), statistics.median(ts)
+                    out.update(bob_us=round(u, 1), bob_ws_us=round(sp, 1),
+                               speedup=round(u / sp, 3), slower=u / sp < 0.98)
+                    slower += int(u / sp < 0.98)
+                    del ws, unsplit, split
+                print(_json.dumps(out), flush=True)
+                del T, a7, O, L, D
+                torch.cuda.empty_cache()
+    print(_json.dumps({"split_audit_shapes": 2 * 2 * len(grid), "slower": slower}), flush=True)
+
+
 def row_sums(args):
     """Cost of the fp32 row-sum option (fbob_bob_ex, FBOB_FLAG_FP32_ROW_SUMS) against the
     default row sums: both through fbob_bob_ex with the workspace the planner asks for,
@@ -705,6 +758,8 @@ def main():
                     help="fbob_bob vs fbob_bob_ws on causal d=64 shapes (HIP-graph timing)")
     ap.add_argument("--n-sweep", action="store_true",
                     help="BoB rate against N at B=1 H=12 d=64 (HIP-graph timing)")
+    ap.add_argument("--split-audit", action="store_true",
+                    help="fbob_bob vs fbob_bob_ws on a grid of shapes (HIP graphs)")
     ap.add_argument("--row-sums", action="store_true",
                     help="cost of fbob_bob_ex's fp32 row sums against the default (HIP graphs)")
     ap.add_argument("--max-n-start", type=int, default=1 << 18)
@@ -757,6 +812,13 @@ def main():
             sys.exit(3)
         fb.load_library()
         n_sweep(args)
+        return
+    if args.split_audit:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(3)
+        fb.load_library()
+        split_audit(args)
         return
     if args.row_sums:
         if not torch.cuda.is_available():

@@ -112,7 +112,7 @@ def test_cpu_baseline_on_a_tiny_workload():
 
 
 @pytest.mark.parametrize("mode", [["--fill-sweep"], ["--causal-ab"], ["--causal-split"], ["--n-sweep"],
-                                  ["--row-sums"],
+                                  ["--row-sums"], ["--split-audit"],
                                   ["--max-n"],
                                   ["--workspace", "--workload", "gpt2_heads_h12_n4096_d64_bf16"]])
 def test_measurement_modes_parse_and_need_a_gpu(mode):
