@@ -647,8 +647,9 @@ def n_sweep(args):
 
 
 def split_audit(args):
-    """Check of the split planner: fbob_bob against fbob_bob_ws (the workspace the
-    planner asks for) on a grid of small and medium shapes (d = 64 and 128, with and
+    """Check of the split planners: fbob_bob against fbob_bob_ws, and fbob_backward against
+    fbob_backward_ws (the workspaces the planners ask for), on a grid of small and medium
+    shapes (d = 64 and 128, with and
     without the mask, 1-20 heads, grouped heads, B up to 3, N 2048-32768), each timed
     as a HIP graph of back-to-back calls, interleaved over three rounds (median).  One
     JSON line per shape; "slower" marks a split that lost more than 2 %."""
@@ -693,6 +694,25 @@ def split_audit(args):
                                speedup=round(u / sp, 3), slower=u / sp < 0.98)
                     slower += int(u / sp < 0.98)
                     del ws, unsplit, split
+                # the first backward's planner (fbob_backward_ws) on the same shape
+                gneed = fb.backward_workspace_size(a7[0], a7[1], w.tau, causal)
+                out["grad_workspace_bytes"] = gneed
+                if gneed > 0:
+                    gws = torch.empty(gneed, dtype=torch.uint8, device="cuda")
+                    pairs = N * (N + 1) / 2 if causal else N * N
+                    reps = max(3, min(40, int(40 * 12 * 4096 ** 2 * 64 / (B * H * pairs * d))))
+                    gu = graph_timed(lambda: fb.backward(*a7[:4], O, L, w.tau, causal), reps)
+                    gs = graph_timed(lambda: fb.backward_ws(*a7[:4], O, L, w.tau, causal,
+                                                            workspace=gws), reps)
+                    tu, ts = [], []
+                    for _ in range(3):
+                        tu.append(gu())
+                        ts.append(gs())
+                    u, sp = statistics.median(tu), statistics.median(ts)
+                    out.update(backward_us=round(u, 1), backward_ws_us=round(sp, 1),
+                               grad_speedup=round(u / sp, 3), grad_slower=u / sp < 0.98)
+                    slower += int(u / sp < 0.98)
+                    del gws, gu, gs
                 print(_json.dumps(out), flush=True)
                 del T, a7, O, L, D
                 torch.cuda.empty_cache()

@@ -10,6 +10,7 @@ in the library's HIP kernels; there is no fallback path.
 Entry points (same names as the C ABI):
     forward(Q, K, V, dO, tau, causal)              -> O, L, D   (dO=None: O, L, None)
     backward(Q, K, V, dO, O, L, tau, causal)       -> dict(dQ, dK, dV, D)
+    backward_ws(..., workspace)                     -> as backward; small problems split
     bob(Q, K, V, dO, UQ, UK, UV, O, L, D, ...)     -> dict(dQt, dKt, dVt, ddOt, alpha, E)
     bob_pass1(...)                                  -> dict(dQt, ddOt, alpha, E)
     bob_pass2(..., alpha, E)                        -> dict(dKt, dVt)
@@ -31,7 +32,8 @@ import os
 
 from ._lib import FbobError, load_library, STATUS  # noqa: F401
 
-__all__ = ["forward", "backward", "bob", "bob_pass1", "bob_pass2", "bob_ws", "bob_ex",
+__all__ = ["forward", "backward", "backward_ws", "backward_workspace_size", "bob", "bob_pass1",
+           "bob_pass2", "bob_ws", "bob_ex",
            "bob_noalloc", "bob_workspace_size", "FLAG_FP32_ROW_SUMS", "load_library",
            "FbobError", "library_path", "version"]
 
@@ -171,6 +173,48 @@ def backward(Q, K, V, dO, O, L, tau=None, causal=False):
     _call(dev, lib.fbob_backward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
           int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L),
           _p(out["dQ"]), _p(out["dK"]), _p(out["dV"]), _p(out["D"]), _stream(dev))
+    return out
+
+
+def backward_workspace_size(Q, K, tau=None, causal=False) -> int:
+    """Bytes of device workspace ``backward_ws`` can use for this problem (C ABI
+    ``fbob_backward_workspace_size``); 0 when the problem fills the GPU unsplit."""
+    lib = load_library()
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    out = ctypes.c_int64(0)
+    st = lib.fbob_backward_workspace_size(_dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+                                          int(bool(causal)), ctypes.byref(out))
+    if st != 0:
+        raise FbobError(st)
+    return int(out.value)
+
+
+def backward_ws(Q, K, V, dO, O, L, tau=None, causal=False, workspace=None):
+    """``backward`` with a caller-owned workspace (C ABI ``fbob_backward_ws``): problems
+    too small to fill the GPU split their sweeps over more work-groups.  ``workspace`` is a
+    contiguous GPU tensor of at least ``backward_workspace_size`` bytes; None allocates
+    one with torch.  Returns the same dict as ``backward``."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO)
+    dev = Q.device
+    _check_f32(O, (B, Hq, N, d), "O", dev)
+    _check_f32(L, (B, Hq, N), "L", dev)
+    if workspace is None:
+        need = backward_workspace_size(Q, K, tau, causal)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
+    nbytes = workspace.numel() * workspace.element_size()
+    out = dict(dQ=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               dK=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               dV=torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev),
+               D=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    _call(dev, lib.fbob_backward_ws, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), _p(O), _p(L),
+          _p(out["dQ"]), _p(out["dK"]), _p(out["dV"]), _p(out["D"]), _p(workspace), nbytes,
+          _stream(dev))
     return out
 
 

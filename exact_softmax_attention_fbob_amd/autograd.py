@@ -5,7 +5,8 @@
     O = attention(Q, K, V, fp32_row_sums=True)           # BoB with fp32 alpha, E'
 
 * forward: ``fbob_forward`` without dO (O and the log-partition L);
-* first backward (dQ, dK, dV for an upstream dO): ``fbob_backward``, which also
+* first backward (dQ, dK, dV for an upstream dO): ``fbob_backward_ws`` (a workspace
+  from torch's allocator, so that small problems split their sweeps), which also
   returns the row scalar D;
 * backward of that backward: for cotangents (U_Q, U_K, U_V) of (dQ, dK, dV) the
   vector-Jacobian product of the first backward is the gradient of
@@ -37,7 +38,7 @@ from __future__ import annotations
 import torch
 
 from . import FLAG_FP32_ROW_SUMS as _FLAG_FP32_ROW_SUMS
-from . import backward as _backward
+from . import backward_ws as _backward
 from . import bob_ex as _bob_ex
 from . import forward as _forward
 

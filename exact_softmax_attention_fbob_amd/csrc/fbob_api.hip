@@ -246,21 +246,44 @@ int fbob_backward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
                   int causal, const void* Q, const void* K, const void* V, const void* dO,
                   const float* O, const float* L, float* dQ, float* dK, float* dV, float* D,
                   void* stream) {
+  return fbob_backward_ws(dtype, B, Hq, Hkv, N, d, tau, causal, Q, K, V, dO, O, L, dQ, dK, dV,
+                          D, nullptr, 0, stream);
+}
+
+int fbob_backward_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                 int64_t d, float tau, int causal, int64_t* bytes) {
+  if (bytes == nullptr) return FBOB_ERR_INVALID_ARG;
   Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
   if (c.status != FBOB_OK) return c.status;
+  *bytes = c.empty ? 0 : fbob::grad_split_plan(c.p).bytes();
+  return FBOB_OK;
+}
+
+int fbob_backward_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     float tau, int causal, const void* Q, const void* K, const void* V,
+                     const void* dO, const float* O, const float* L, float* dQ, float* dK,
+                     float* dV, float* D, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (workspace_bytes < 0) return FBOB_ERR_INVALID_ARG;
   if (c.empty) return FBOB_OK;
+  const fbob::GradPlan plan = fbob::grad_split_plan(c.p);
+  // the split schedule only with a workspace that holds its partial sums
+  const bool split = plan.bytes() > 0 && workspace != nullptr && workspace_bytes >= plan.bytes();
   const int64_t es = c.p.bf16 ? 2 : 4;
   const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
   const int64_t ob = B * Hq * N * d * 4, kob = B * Hkv * N * d * 4, rb = B * Hq * N * 4;
   const void* ins[] = {Q, K, V, dO, O, L};
   const int64_t inb[] = {qb, kb, kb, qb, ob, rb};
-  void* outs[] = {dQ, dK, dV, D};
-  const int64_t outb[] = {ob, kob, kob, rb};
-  const int st = check_ptrs(ins, inb, 6, outs, outb, 4);
+  void* outs[] = {dQ, dK, dV, D, split ? workspace : nullptr};
+  const int64_t outb[] = {ob, kob, kob, rb, plan.bytes()};
+  const int st = check_ptrs(ins, inb, 6, outs, outb, split ? 5 : 4);
   if (st != FBOB_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   fbob::GradArgs a{Q, K, V, dO, O, L, dQ, dK, dV, D};
   clear_pending();
+  if (split) return finish(fbob::launch_backward_split(c.p, a, plan, workspace, s));
   const int st1 = finish(fbob::launch_grad_dq(c.p, a, s));
   if (st1 != FBOB_OK) return st1;
   return finish(fbob::launch_grad_dkv(c.p, a, s));

@@ -33,7 +33,8 @@ namespace {
 // columns 16 db + 4 g .. +3 of its row).  D_i is formed from the resident dO
 // fragments and the fp32 O rows first.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int BC, bool DIRECT, bool CAUSAL, int NI = 1>
+template <typename T, int D, int NW, int BC, bool DIRECT, bool CAUSAL, int NI = 1,
+          bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, int group, int N,
                                                           float tau, int n_row_tiles, int total) {
   using E = Elem<T>;
@@ -50,9 +51,12 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bh = logical / n_row_tiles;
+  // SPLIT: the parts of one row tile are consecutive work-groups (one XCD).
+  const int split = SPLIT ? logical % a.nsplit : 0;
+  const int lt = SPLIT ? logical / a.nsplit : logical;
+  const int bh = lt / n_row_tiles;
   // Causal: the last row tiles see the most keys, so they are dispatched first.
-  const int rt = CAUSAL ? n_row_tiles - 1 - logical % n_row_tiles : logical % n_row_tiles;
+  const int rt = CAUSAL ? n_row_tiles - 1 - lt % n_row_tiles : lt % n_row_tiles;
   const int b = bh / Hq, h = bh % Hq, hk = h / group;
   const int64_t q_off = (int64_t)bh * N * D;
   const int64_t kv_off = ((int64_t)b * (Hq / group) + hk) * N * D;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
     }
     dv[ib] = group_sum(dpart);  // D_i: the 4 lanes of row r hold 8 columns each
     nl2[ib] = i < N ? -a.L[(int64_t)bh * N + i] * kLog2e : 0.f;
-    if (i < N && g == 0) a.D[(int64_t)bh * N + i] = dv[ib];
+    if (i < N && g == 0 && split == 0) a.D[(int64_t)bh * N + i] = dv[ib];
   }
 
   f32x4 accX[NI][kDB];
@@ -97,6 +101,13 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
 
   const int jend = CAUSAL ? min(N, rt * kBR + kBR) : N;
   const int ntc = (jend + BC - 1) / BC;
+  // this work-group's key stages [t_lo, t_hi): all of them, or its part's share
+  int t_lo = 0, t_hi = ntc;
+  if constexpr (SPLIT) {
+    const int per = (ntc + a.nsplit - 1) / a.nsplit;
+    t_lo = min(ntc, split * per);
+    t_hi = min(ntc, t_lo + per);
+  }
 
   // 32 keys at j0 from the staged K tile Kt (V tile follows it).
   auto half = [&](const char* Kt, int j0) {
@@ -160,13 +171,15 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
     if constexpr (DIRECT) wait_all_memory();
     else st.store(buf);
   };
-  stage_load(lds[0], 0);
-  stage_commit(lds[0]);
+  if (!SPLIT || t_lo < t_hi) {  // (an empty part stages nothing)
+    stage_load(lds[0], t_lo * BC);
+    stage_commit(lds[0]);
+  }
   __syncthreads();
 
   auto step = [&](int t, char* cur, char* nxt) {
     const int j0 = t * BC;
-    const bool more = t + 1 < ntc;
+    const bool more = t + 1 < t_hi;
     if (more) stage_load(nxt, j0 + BC);
 #pragma unroll
     for (int hs = 0; hs < BC / 32; ++hs) {
@@ -177,15 +190,21 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
     __syncthreads();
   };
 #pragma unroll 1
-  for (int t = 0; t < ntc; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     step(t, lds[0], lds[1]);
-    if (t + 1 < ntc) step(t + 1, lds[1], lds[0]);
+    if (t + 1 < t_hi) step(t + 1, lds[1], lds[0]);
   }
 
 #pragma unroll
   for (int ib = 0; ib < NI; ++ib) {
     const int i = iw0 + 16 * ib + r;
-    if (i < N) {
+    if (SPLIT && i < N) {  // this part's tau dQ (zeros for an empty part)
+      const int64_t heads = (int64_t)gridDim.x / ((int64_t)n_row_tiles * a.nsplit);
+      float* pp = a.part + (((int64_t)split * heads + bh) * N + i) * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+        *reinterpret_cast<f32x4*>(pp + 16 * db + 4 * g) = tau * accX[ib][db];
+    } else if (i < N) {
       const int64_t ro = q_off + (int64_t)i * D;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
@@ -200,7 +219,8 @@ __global__ __launch_bounds__(NW * 64) void grad_dq_kernel(GradArgs a, int Hq, in
 // -D through LDS for every query head of the group, and accumulates
 // dK^T += Q^T dS and dV^T += dO^T P with the score C registers as B operands.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int NJ, int BRS, bool DIRECT, bool CAUSAL>
+template <typename T, int D, int NW, int NJ, int BRS, bool DIRECT, bool CAUSAL,
+          bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, int group, int N,
                                                            float tau, int n_col_tiles, int total) {
   using E = Elem<T>;
@@ -219,7 +239,10 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bhk = logical / n_col_tiles, ct = logical % n_col_tiles;
+  // SPLIT: the parts of one column tile are consecutive work-groups (one XCD).
+  const int split = SPLIT ? logical % a.nsplit : 0;
+  const int lt = SPLIT ? logical / a.nsplit : logical;
+  const int bhk = lt / n_col_tiles, ct = lt % n_col_tiles;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int Hq = Hkv * group;
   const int64_t kv_off = (int64_t)bhk * N * D;
@@ -250,6 +273,13 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
   const int i_begin = CAUSAL ? (ct * kBCw / BRS) * BRS : 0;
   const int nrc = (N - i_begin + BRS - 1) / BRS;
   const int nsteps = nrc * group;
+  // this work-group's steps [t_lo, t_hi): all of them, or its part's share
+  int t_lo = 0, t_hi = nsteps;
+  if constexpr (SPLIT) {
+    const int per = (nsteps + a.nsplit - 1) / a.nsplit;
+    t_lo = min(nsteps, split * per);
+    t_hi = min(nsteps, t_lo + per);
+  }
   const int64_t q_head = (int64_t)N * D * (int64_t)sizeof(T);
   const int64_t q0 = ((int64_t)b * Hq + (int64_t)hk * group) * N * D;
   const T* const q_bases[2] = {reinterpret_cast<const T*>(a.Q) + q0,
@@ -267,6 +297,10 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
   // Steps run in order: the next one to load is query head ld_hq, row chunk ld_rc
   // (advanced by one chunk per load rather than divided out of the step index).
   int ld_hq = 0, ld_rc = 0, nxt_i0 = 0;
+  if constexpr (SPLIT) {  // the part's first step (one division, before the sweep)
+    ld_hq = t_lo / nrc;
+    ld_rc = t_lo - ld_hq * nrc;
+  }
   auto load_step = [&](char* buf) {
     const int hq = ld_hq;
     const int i0 = i_begin + ld_rc * BRS;
@@ -357,14 +391,16 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
     FBOB_PRIO_LOW();
   };
 
-  load_step(lds[0]);
-  if constexpr (DIRECT) wait_all_memory();
-  store_step(lds[0]);
+  if (!SPLIT || t_lo < t_hi) {  // (an empty part stages nothing)
+    load_step(lds[0]);
+    if constexpr (DIRECT) wait_all_memory();
+    store_step(lds[0]);
+  }
   __syncthreads();
   int cur_i0 = nxt_i0;
   auto step = [&](int t, char* cur, char* nxt) {
     const int i0 = cur_i0;
-    const bool more = t + 1 < nsteps;
+    const bool more = t + 1 < t_hi;
     if (more) load_step(nxt);
 #pragma unroll
     for (int sc = 0; sc < BRS / 32; ++sc) {
@@ -379,15 +415,24 @@ __global__ __launch_bounds__(NW * 64) void grad_dkv_kernel(GradArgs a, int Hkv, 
     cur_i0 = nxt_i0;
   };
 #pragma unroll 1
-  for (int t = 0; t < nsteps; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     step(t, lds[0], lds[1]);
-    if (t + 1 < nsteps) step(t + 1, lds[1], lds[0]);
+    if (t + 1 < t_hi) step(t + 1, lds[1], lds[0]);
   }
 
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
     const int j = jw0 + 16 * jb + r;
-    if (j < N) {
+    if (SPLIT && j < N) {  // this part's tau dK, dV (zeros for an empty part)
+      const int64_t heads = (int64_t)gridDim.x / ((int64_t)n_col_tiles * a.nsplit);
+      float* pp = a.part + (((int64_t)split * heads + bhk) * N + j) * 2 * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int d0 = 16 * db + 4 * g;
+        *reinterpret_cast<f32x4*>(pp + d0) = tau * accK[jb][db];
+        *reinterpret_cast<f32x4*>(pp + D + d0) = accV[jb][db];
+      }
+    } else if (j < N) {
       const int64_t ro = kv_off + (int64_t)j * D;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
@@ -429,7 +474,48 @@ hipError_t launch_dkv(const Problem& p, const GradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int NW, int BC, bool DIRECT, int NI>
+hipError_t launch_dq_split(const Problem& p, const GradArgs& a, hipStream_t s) {
+  constexpr int kBR = NW * 16 * NI;
+  const int n_row_tiles = (p.N + kBR - 1) / kBR;
+  const int total = n_row_tiles * p.B * p.Hq * a.nsplit;
+  const int group = p.Hq / p.Hkv;
+  if (p.causal)
+    hipLaunchKernelGGL((grad_dq_kernel<T, D, NW, BC, DIRECT, true, NI, true>), dim3(total),
+                       dim3(NW * 64), 0, s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
+  else
+    hipLaunchKernelGGL((grad_dq_kernel<T, D, NW, BC, DIRECT, false, NI, true>), dim3(total),
+                       dim3(NW * 64), 0, s, a, p.Hq, group, p.N, p.tau, n_row_tiles, total);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int NW, int NJ, int BRS, bool DIRECT>
+hipError_t launch_dkv_split(const Problem& p, const GradArgs& a, hipStream_t s) {
+  constexpr int kBCw = NW * 16 * NJ;
+  const int n_col_tiles = (p.N + kBCw - 1) / kBCw;
+  const int total = n_col_tiles * p.B * p.Hkv * a.nsplit;
+  const int group = p.Hq / p.Hkv;
+  if (p.causal)
+    hipLaunchKernelGGL((grad_dkv_kernel<T, D, NW, NJ, BRS, DIRECT, true, true>), dim3(total),
+                       dim3(NW * 64), 0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
+  else
+    hipLaunchKernelGGL((grad_dkv_kernel<T, D, NW, NJ, BRS, DIRECT, false, true>), dim3(total),
+                       dim3(NW * 64), 0, s, a, p.Hkv, group, p.N, p.tau, n_col_tiles, total);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// The shipped bf16 layouts of the two passes below, in split form (bf16 only).
+hipError_t launch_grad_dq_split(const Problem& p, const GradArgs& a, hipStream_t s) {
+  if (p.d == 64) return launch_dq_split<__bf16, 64, 8, 128, true, 2>(p, a, s);
+  return launch_dq_split<__bf16, 128, 8, 64, true, 2>(p, a, s);
+}
+
+hipError_t launch_grad_dkv_split(const Problem& p, const GradArgs& a, hipStream_t s) {
+  if (p.d == 64) return launch_dkv_split<__bf16, 64, 8, 2, 64, true>(p, a, s);
+  return launch_dkv_split<__bf16, 128, 8, 1, 32, true>(p, a, s);
+}
 
 hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s) {
   if (p.bf16) {

@@ -84,6 +84,11 @@ struct GradArgs {
   const void *Q, *K, *V, *dO;
   const float *O, *L;
   float *dQ, *dK, *dV, *D;
+  // Split sweeps (small grids): the row pass writes part[s][B Hq][N][d] (tau dQ of
+  // split s), the column pass part[s][B Hkv][N][2][d] (tau dK, dV); split s covers the
+  // s-th of nsplit equal shares of a work-group's key stages or row steps.
+  float* part = nullptr;
+  int nsplit = 1;
 };
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
@@ -94,5 +99,17 @@ hipError_t launch_pass2_split(const Problem& p, const Pass2Args& a, hipStream_t 
 hipError_t launch_pass2(const Problem& p, const Pass2Args& a, hipStream_t s);
 hipError_t launch_grad_dq(const Problem& p, const GradArgs& a, hipStream_t s);
 hipError_t launch_grad_dkv(const Problem& p, const GradArgs& a, hipStream_t s);
+// Split forms (a.part, a.nsplit set; bf16 only) and the plan that picks them: the row
+// pass in s1 parts, the column pass in s2 (1 = no split), one workspace of bytes().
+hipError_t launch_grad_dq_split(const Problem& p, const GradArgs& a, hipStream_t s);
+hipError_t launch_grad_dkv_split(const Problem& p, const GradArgs& a, hipStream_t s);
+struct GradPlan {
+  int s1 = 1, s2 = 1;
+  int64_t bytes1 = 0, bytes2 = 0;  // the two passes reuse one buffer
+  int64_t bytes() const { return bytes1 > bytes2 ? bytes1 : bytes2; }
+};
+GradPlan grad_split_plan(const Problem& p);
+hipError_t launch_backward_split(const Problem& p, const GradArgs& a, const GradPlan& plan,
+                                 void* workspace, hipStream_t s);
 
 }  // namespace fbob

@@ -95,6 +95,21 @@ __global__ __launch_bounds__(256) void reduce_pass2_kernel(Pass2Args a, int64_t 
   *reinterpret_cast<f32x4*>(a.dVt + row * D + d0) = v;
 }
 
+// First backward, row pass: dQ = the sum of the parts' tau dQ (one thread per 4
+// consecutive d values of one row).
+template <int D>
+__global__ __launch_bounds__(256) void reduce_dq_kernel(GradArgs a, int64_t rows, int nsplit) {
+  constexpr int kChunks = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / kChunks;  // flat (b, h, i)
+  if (row >= rows) return;
+  const int d0 = 4 * (int)(idx % kChunks);
+  f32x4 q = splat4(0.f);
+  for (int s = 0; s < nsplit; ++s)
+    q += *reinterpret_cast<const f32x4*>(a.part + ((int64_t)s * rows + row) * D + d0);
+  *reinterpret_cast<f32x4*>(a.dQ + row * D + d0) = q;
+}
+
 // Parts s in {1, 2, 4, 8} for `units` work-groups whose full sweep takes `sweep_us`
 // and has `stages` stages (at least two per part), with `part_bytes` of partial sums
 // per part.  Estimated time: the rounds of work-groups over the CUs, each 1/s of a
@@ -368,6 +383,89 @@ hipError_t launch_bob_split(const Problem& p, const Pass1Args& a1_in, const Pass
     return hipGetLastError();
   }
   return launch_pass2(p, a2_in, s);
+}
+
+// The first backward's passes split like the BoB's (uniform parts): the row pass owns
+// 256 query rows per work-group (128-key stages at d = 64, 64 at d = 128), the column
+// pass 256 keys (d = 64, 64-row steps) or 128 (d = 128, 32-row steps).  With the causal
+// mask (tiles single, longest first) and at d = 128 a pass splits only while its tiles
+// do not fill one round of the CUs.
+GradPlan grad_split_plan(const Problem& p) {
+  GradPlan plan;
+  if (!p.bf16) return plan;
+  const int64_t heads_q = (int64_t)p.B * p.Hq, heads_kv = (int64_t)p.B * p.Hkv;
+  const int64_t group = p.Hq / p.Hkv;
+  const int row_tile = 256, bc = p.d == 64 ? 128 : 64;
+  const int col_tile = p.d == 64 ? 256 : 128, brs = p.d == 64 ? 64 : 32;
+  const int64_t row_tiles = (p.N + row_tile - 1) / row_tile;
+  const int64_t col_tiles = (p.N + col_tile - 1) / col_tile;
+  int64_t stages1 = (p.N + bc - 1) / bc;
+  int64_t steps2 = (p.N + brs - 1) / brs * group;
+  if (p.causal) {  // the mean tile
+    stages1 = std::max<int64_t>(1, (stages1 + 1) / 2);
+    steps2 = std::max<int64_t>(1, (steps2 + 1) / 2);
+  }
+  const int64_t units1 = row_tiles * heads_q, units2 = col_tiles * heads_kv;
+  // sweep times per 32 keys (row pass) or 32 rows (column pass) of one work-group, from
+  // the passes at B=1 H=12 N=16384 d=64 (1.08 ms and 1.45 ms for 3 rounds): ~0.7 and
+  // ~0.94 us, about twice that at d = 128
+  const double sweep1 = (p.d == 64 ? 0.7 : 1.4) * bc / 32.0 * stages1;
+  const double sweep2 = (p.d == 64 ? 0.94 : 1.9) * brs / 32.0 * steps2;
+  // Causal tiles, and every tile at d = 128, split only while a pass's tiles do not fill
+  // one round (d = 128, B=1 H=20 N=4096: 320 and 640 tiles, split anyway 705 -> 758 us;
+  // at d = 64 splits past one round still gained 5-12 %).
+  const bool round_only = p.causal || p.d == 128;
+  if (!round_only || units1 < kCUs) {
+    plan.s1 = choose_parts(units1, stages1, sweep1, (double)heads_q * p.N * p.d * 4);
+    if (plan.s1 > 1) plan.bytes1 = (int64_t)plan.s1 * heads_q * p.N * p.d * 4;
+  }
+  if (!round_only || units2 < kCUs) {
+    plan.s2 = choose_parts(units2, steps2, sweep2, (double)heads_kv * p.N * 2 * p.d * 4);
+    if (plan.s2 > 1) plan.bytes2 = (int64_t)plan.s2 * heads_kv * p.N * 2 * p.d * 4;
+  }
+  return plan;
+}
+
+hipError_t launch_backward_split(const Problem& p, const GradArgs& a_in, const GradPlan& plan,
+                                 void* workspace, hipStream_t s) {
+  float* ws = static_cast<float*>(workspace);
+  if (plan.s1 > 1) {
+    GradArgs a = a_in;
+    a.part = ws;
+    a.nsplit = plan.s1;
+    hipError_t e = launch_grad_dq_split(p, a, s);
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)p.B * p.Hq * p.N;
+    const dim3 grid((unsigned)((rows * (p.d / 4) + 255) / 256));
+    if (p.d == 64)
+      hipLaunchKernelGGL(reduce_dq_kernel<64>, grid, dim3(256), 0, s, a, rows, plan.s1);
+    else
+      hipLaunchKernelGGL(reduce_dq_kernel<128>, grid, dim3(256), 0, s, a, rows, plan.s1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const hipError_t e = launch_grad_dq(p, a_in, s);
+    if (e != hipSuccess) return e;
+  }
+  if (plan.s2 > 1) {  // after the row pass (it reads D, and reuses the workspace)
+    GradArgs a = a_in;
+    a.part = ws;
+    a.nsplit = plan.s2;
+    hipError_t e = launch_grad_dkv_split(p, a, s);
+    if (e != hipSuccess) return e;
+    Pass2Args r{};  // the BoB's Pass 2 reduction: the same part layout
+    r.part = ws;
+    r.dKt = a_in.dK;
+    r.dVt = a_in.dV;
+    const int64_t rows = (int64_t)p.B * p.Hkv * p.N;
+    const dim3 grid((unsigned)((rows * (p.d / 4) + 255) / 256));
+    if (p.d == 64)
+      hipLaunchKernelGGL(reduce_pass2_kernel<64>, grid, dim3(256), 0, s, r, rows, plan.s2);
+    else
+      hipLaunchKernelGGL(reduce_pass2_kernel<128>, grid, dim3(256), 0, s, r, rows, plan.s2);
+    return hipGetLastError();
+  }
+  return launch_grad_dkv(p, a_in, s);
 }
 
 }  // namespace fbob

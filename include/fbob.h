@@ -114,6 +114,40 @@ int fbob_backward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
                   float* dQ, float* dK, float* dV, float* D, void* stream);
 
 /*
+ * Device workspace, in bytes, that fbob_backward_ws can use for this problem (0 when the
+ * problem fills the GPU without splitting: then fbob_backward_ws is fbob_backward).  Same
+ * size arguments as fbob_backward; writes the size to *bytes.  FBOB_ERR_INVALID_ARG if
+ * bytes is NULL; size errors as fbob_backward.  No HIP call.
+ */
+int fbob_backward_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                 int64_t d, float tau, int causal, int64_t* bytes);
+
+/*
+ * fbob_backward with a caller-owned device workspace for problems too small to fill the
+ * GPU (the same split schedule as fbob_bob_ws, FlashBoB notes, "关键设计" 2): a row-pass
+ * work-group owns 256 query rows and a column-pass work-group 256 keys (d = 64) or 128
+ * (d = 128); when a pass has too few of them for the 256 CUs, each one's key sweep or
+ * row sweep is split over 2-8 work-groups that write fp32 partial sums to the workspace,
+ * and a reduction adds them in a fixed order (deterministic; the results differ from
+ * fbob_backward's only by the order of the fp32 additions) and writes every output once.
+ * bf16 inputs; with causal != 0 or at d = 128 a pass splits only while its tiles do not
+ * fill one round of the CUs (unequal tiles dispatched longest first already balance, and
+ * at d = 128 splits past one round measured slower).
+ *   workspace       DEVICE pointer, 16-byte aligned, owned by the caller, at least
+ *                   fbob_backward_workspace_size() bytes; NULL (or fewer bytes) runs
+ *                   exactly fbob_backward.  Contents on entry ignored, on return
+ *                   undefined; must not overlap any other argument (FBOB_ERR_ALIAS).
+ *                   Calls sharing one workspace must be ordered (same stream).
+ * Other arguments, outputs and errors as fbob_backward.
+ */
+int fbob_backward_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                     float tau, int causal,
+                     const void* Q, const void* K, const void* V, const void* dO,
+                     const float* O, const float* L,
+                     float* dQ, float* dK, float* dV, float* D,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Exact BoB: Pass 1 then Pass 2 on the same stream (FlashBoB notes,
  * "整体框架" flowchart and "关键设计" 2).  No N x N tensor is written to memory;
  * alpha and E are the only state that crosses from Pass 1 to Pass 2.

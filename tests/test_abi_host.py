@@ -36,7 +36,8 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
-        ["fbob_forward", "fbob_backward", "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
+        ["fbob_forward", "fbob_backward", "fbob_backward_ws", "fbob_backward_workspace_size",
+         "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
          "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_bob_ex", "fbob_bob_noalloc",
          "fbob_strerror", "fbob_hip_error_string", "fbob_version"])
     assert sorted(_lib.PROTOTYPES) == declared_functions()
@@ -299,6 +300,40 @@ def test_status_names_cover_every_code(lib):
     text = open(HEADER).read()
     for code, name in _lib.STATUS.items():
         assert f"{name} = {code}" in text, name
+
+
+def test_backward_workspace_size_and_validation(lib):
+    """fbob_backward_workspace_size follows the first backward's split plan (B=1 H=12
+    N=4096 d=64: 192 row-pass and 192 column-pass work-groups on 256 CUs); problems that
+    fill the GPU, fp32 and causal problems whose tiles fill a round need none; validation
+    as fbob_backward, plus the workspace's own."""
+    def bws(dtype=1, B=1, Hq=12, Hkv=12, N=4096, d=64, causal=0):
+        out = ctypes.c_int64(-1)
+        st = lib.fbob_backward_workspace_size(dtype, B, Hq, Hkv, N, d, ctypes.c_float(0.125),
+                                              causal, ctypes.byref(out))
+        return st, out.value
+    st, b = bws(Hq=2, Hkv=2)
+    assert st == OK and b > 0
+    assert bws(N=16384) == (OK, 0)
+    assert bws(dtype=0, Hq=2, Hkv=2) == (OK, 0)
+    assert bws(N=0) == (OK, 0)
+    assert bws(d=96)[0] == UNSUPPORTED
+    assert lib.fbob_backward_workspace_size(1, 1, 1, 1, 64, 64, ctypes.c_float(0.125), 0,
+                                            None) == INVALID
+    fb = FakeBuffers(11)
+    ptrs = [fb[m] for m in range(10)]
+    need = bws(Hq=2, Hkv=2)[1]
+
+    def call(ws, nbytes, p=ptrs, N=4096):
+        return lib.fbob_backward_ws(1, 1, 2, 2, N, 64, ctypes.c_float(0.125), 0, *p, ws,
+                                    nbytes, ctypes.c_void_p(0))
+    assert call(fb[10], -1) == INVALID
+    assert call(ctypes.c_void_p(fb.addrs[6] + 64), need) == ALIAS      # inside dQ
+    assert call(ctypes.c_void_p(fb.addrs[10] + 8), need) == ALIGN
+    assert call(fb[10], need, N=0) == OK
+    bad = list(ptrs)
+    bad[2] = ctypes.c_void_p(0)
+    assert call(fb[10], need, p=bad) == INVALID
 
 
 def test_header_states_the_scratch_size():

@@ -292,3 +292,45 @@ def test_autograd_hessian_vector_product_of_squared_output():
     errs = U.compare_full(got, ref, w, keys=("dQt", "dKt", "dVt"))
     U.say(f"[autograd] {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
+
+
+# ---------------------------------------------------------------------------
+# split schedule of the first backward (fbob_backward_ws) on problems too small to fill
+# the GPU: against the oracle, against the unsplit call, and bitwise repeatable
+# ---------------------------------------------------------------------------
+
+SPLIT_GRAD = [
+    case("gws_n1000_h2_ragged", 1, 2, 1000, 64, "bf16", 91),
+    case("gws_gqa_hq8_hkv2_n700", 1, 8, 700, 64, "bf16", 92, Hkv=2),
+    case("gws_n1500_h2_d128", 1, 2, 1500, 128, "bf16", 93),
+    case("gws_causal_n1000_h2", 1, 2, 1000, 64, "bf16", 94, causal=True),
+    case("gws_causal_gqa_hq6_hkv2_n600_d128", 1, 6, 600, 128, "bf16", 95, causal=True, Hkv=2),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT_GRAD, ids=[w.name for w in SPLIT_GRAD])
+def test_backward_split_schedule(w):
+    import torch
+    import exact_softmax_attention_fbob_amd as fb
+    U.say(f"[grad] split {w.name}")
+    inp = U.make_inputs(w)
+    dev = U.to_device(inp, w.dtype)
+    Q, K, V, dO = (dev[k] for k in ("Q", "K", "V", "dO"))
+    O, L, _ = fb.forward(Q, K, V, None, w.tau, w.causal)
+    need = fb.backward_workspace_size(Q, K, w.tau, w.causal)
+    assert need > 0, "the case is meant to take the split schedule"
+    ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    got = fb.backward_ws(Q, K, V, dO, O, L, w.tau, w.causal, workspace=ws)
+    again = fb.backward_ws(Q, K, V, dO, O, L, w.tau, w.causal, workspace=ws)
+    ref = fb.backward(Q, K, V, dO, O, L, w.tau, w.causal)
+    torch.cuda.synchronize()
+    for k in got:
+        assert torch.equal(got[k], again[k]), k
+    diff = {k: float((got[k] - ref[k]).abs().max() / ref[k].abs().max()) for k in got}
+    U.say(f"[grad] split {w.name} vs unsplit: " + " ".join(f"{k}={v:.1e}" for k, v in diff.items()))
+    assert all(v < 3e-3 for v in diff.values()), diff
+    assert torch.equal(got["D"], ref["D"])
+    gpu = {k: v.cpu().numpy().astype(np.float64) for k, v in got.items()}
+    errs = compare(gpu, oracle_grad(inp, w), w)
+    U.say(f"[grad] split {w.name} vs oracle: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= U.TOL[w.dtype] for v in errs.values()), errs
