@@ -1,7 +1,8 @@
 """GPU parity on seeded random configurations: combinations of batch, grouped heads,
 length (tiny, ragged, several tiles), head size, mask, tau, input scale and storage
 type that the hand-picked cases do not cover one by one.  A second, wider draw of 150
-runs every BoB entry point (the fp32 row-sum option and the static-scratch form too).
+runs every BoB entry point (the fp32 row-sum option and the static-scratch form too) and
+the first backward's split form.
 
 Every configuration runs the forward, the BoB (``fbob_bob``, and ``fbob_bob_ws`` with
 the workspace the planner asks for) and the first backward through the C ABI and
@@ -133,7 +134,8 @@ def test_random_configuration_matches_oracle(w):
 @pytest.mark.parametrize("w", WIDE, ids=[w.name for w in WIDE])
 def test_wide_random_configuration_every_bob_entry_point(w):
     """fbob_bob, fbob_bob_ws, fbob_bob_ex with fp32 row sums and fbob_bob_noalloc (where
-    the split fits the static scratch) against the oracle, every output element."""
+    the split fits the static scratch), and the first backward through fbob_backward_ws,
+    against the oracle, every output element."""
     import torch
     import exact_softmax_attention_fbob_amd as fb
     U.say(f"[wide] {w.name}")
@@ -155,6 +157,25 @@ def test_wide_random_configuration_every_bob_entry_point(w):
                    D=D.cpu().numpy().astype(np.float64))
         keys = U.ALL_KEYS + (("O", "L", "D") if kind == "bob" else ())
         errs.update({f"{kind}.{k}": v for k, v in U.compare_full(got, ref, w, keys=keys).items()})
+    # the first backward through fbob_backward_ws (split where its planner splits)
+    g = fb.backward_ws(*a7[:4], O, L, w.tau, w.causal)
+    gd = {kk: v.cpu().numpy().astype(np.float64) for kk, v in g.items()}
+    q, k = U.split_inputs(inp, w)
+    gq, gk, gv = [], {}, {}
+    for (b, h) in U.head_list(w):
+        dQ, dK, dV = oracle.first_backward(q("Q", b, h), k("K", b, h), k("V", b, h),
+                                           q("dO", b, h), w.tau, w.causal)
+        gq.append((b, h, dQ))
+        key = (b, U.kv_index(w, h))
+        gk[key] = gk.get(key, 0) + dK
+        gv[key] = gv.get(key, 0) + dV
+    errs["grad_ws.dQ"] = U.rel(np.stack([gd["dQ"][b, h] for b, h, _ in gq]),
+                               np.stack([x for _, _, x in gq]))
+    keys = sorted(gk)
+    errs["grad_ws.dK"] = U.rel(np.stack([gd["dK"][b, j] for b, j in keys]),
+                               np.stack([gk[kk] for kk in keys]))
+    errs["grad_ws.dV"] = U.rel(np.stack([gd["dV"][b, j] for b, j in keys]),
+                               np.stack([gv[kk] for kk in keys]))
     top = max(errs, key=errs.get)
     U.say(f"[wide] {w.name}: worst {top}={errs[top]:.2e}")
     bad = {kk: v for kk, v in errs.items() if not (v <= U.TOL[w.dtype])}
