@@ -647,8 +647,9 @@ def n_sweep(args):
 
 
 def split_audit(args):
-    """Check of the split planners: fbob_bob against fbob_bob_ws, and fbob_backward against
-    fbob_backward_ws (the workspaces the planners ask for), on a grid of small and medium
+    """Check of the split planners: fbob_bob against fbob_bob_ws, fbob_backward against
+    fbob_backward_ws and fbob_forward against fbob_forward_ws (the workspaces the planners
+    ask for), on a grid of small and medium
     shapes (d = 64 and 128, with and
     without the mask, 1-20 heads, grouped heads, B up to 3, N 2048-32768), each timed
     as a HIP graph of back-to-back calls, interleaved over three rounds (median).  One
@@ -713,6 +714,25 @@ def split_audit(args):
                                grad_speedup=round(u / sp, 3), grad_slower=u / sp < 0.98)
                     slower += int(u / sp < 0.98)
                     del gws, gu, gs
+                # the forward's planner (fbob_forward_ws) on the same shape
+                fneed = fb.forward_workspace_size(a7[0], a7[1], w.tau, causal)
+                out["fwd_workspace_bytes"] = fneed
+                if fneed > 0:
+                    fws = torch.empty(fneed, dtype=torch.uint8, device="cuda")
+                    pairs = N * (N + 1) / 2 if causal else N * N
+                    reps = max(3, min(100, int(100 * 12 * 4096 ** 2 * 64 / (B * H * pairs * d))))
+                    fu = graph_timed(lambda: fb.forward(*a7[:4], w.tau, causal), reps)
+                    fs = graph_timed(lambda: fb.forward_ws(*a7[:4], w.tau, causal,
+                                                           workspace=fws), reps)
+                    tu, ts = [], []
+                    for _ in range(3):
+                        tu.append(fu())
+                        ts.append(fs())
+                    u, sp = statistics.median(tu), statistics.median(ts)
+                    out.update(forward_us=round(u, 1), forward_ws_us=round(sp, 1),
+                               fwd_speedup=round(u / sp, 3), fwd_slower=u / sp < 0.98)
+                    slower += int(u / sp < 0.98)
+                    del fws, fu, fs
                 print(_json.dumps(out), flush=True)
                 del T, a7, O, L, D
                 torch.cuda.empty_cache()

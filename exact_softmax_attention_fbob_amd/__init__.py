@@ -32,8 +32,8 @@ import os
 
 from ._lib import FbobError, load_library, STATUS  # noqa: F401
 
-__all__ = ["forward", "backward", "backward_ws", "backward_workspace_size", "bob", "bob_pass1",
-           "bob_pass2", "bob_ws", "bob_ex",
+__all__ = ["forward", "forward_ws", "forward_workspace_size", "backward", "backward_ws",
+           "backward_workspace_size", "bob", "bob_pass1", "bob_pass2", "bob_ws", "bob_ex",
            "bob_noalloc", "bob_workspace_size", "FLAG_FP32_ROW_SUMS", "load_library",
            "FbobError", "library_path", "version"]
 
@@ -150,6 +150,44 @@ def forward(Q, K, V, dO=None, tau=None, causal=False):
     _call(Q.device, lib.fbob_forward, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
           int(bool(causal)), _p(Q), _p(K), _p(V), None if dO is None else _p(dO), _p(O), _p(L),
           None if D is None else _p(D), _stream(Q.device))
+    return O, L, D
+
+
+def forward_workspace_size(Q, K, tau=None, causal=False) -> int:
+    """Bytes of device workspace ``forward_ws`` can use for this problem (C ABI
+    ``fbob_forward_workspace_size``); 0 when the problem fills the GPU unsplit."""
+    lib = load_library()
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    out = ctypes.c_int64(0)
+    st = lib.fbob_forward_workspace_size(_dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+                                         int(bool(causal)), ctypes.byref(out))
+    if st != 0:
+        raise FbobError(st)
+    return int(out.value)
+
+
+def forward_ws(Q, K, V, dO=None, tau=None, causal=False, workspace=None):
+    """``forward`` with a caller-owned workspace (C ABI ``fbob_forward_ws``): problems too
+    small to fill the GPU split each row tile's key sweep over more work-groups.
+    ``workspace`` is a contiguous GPU tensor of at least ``forward_workspace_size`` bytes;
+    None allocates one with torch.  Returns (O, L, D) like ``forward``."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Hkv, N, d = _check_inputs(Q, K, V, dO)
+    dev = Q.device
+    if workspace is None:
+        need = forward_workspace_size(Q, K, tau, causal)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
+    nbytes = workspace.numel() * workspace.element_size()
+    O = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    L = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    D = None if dO is None else torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    _call(dev, lib.fbob_forward_ws, _dtype_code(Q), B, Hq, Hkv, N, d, _tau(tau, d),
+          int(bool(causal)), _p(Q), _p(K), _p(V), None if dO is None else _p(dO), _p(O), _p(L),
+          None if D is None else _p(D), _p(workspace), nbytes, _stream(dev))
     return O, L, D
 
 

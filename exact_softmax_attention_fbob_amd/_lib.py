@@ -23,6 +23,8 @@ _SIZES = [_i, _i64, _i64, _i64, _i64, _i64, _f, _i]  # dtype, B, Hq, Hkv, N, d, 
 PROTOTYPES = {
     "fbob_forward": (_i, _SIZES + [_vp] * 4 + [_vp] * 3 + [_vp]),
     "fbob_backward": (_i, _SIZES + [_vp] * 4 + [_vp] * 2 + [_vp] * 4 + [_vp]),
+    "fbob_forward_workspace_size": (_i, _SIZES + [ctypes.POINTER(_i64)]),
+    "fbob_forward_ws": (_i, _SIZES + [_vp] * 4 + [_vp] * 3 + [_vp, _i64] + [_vp]),
     "fbob_backward_workspace_size": (_i, _SIZES + [ctypes.POINTER(_i64)]),
     "fbob_backward_ws": (_i, _SIZES + [_vp] * 4 + [_vp] * 2 + [_vp] * 4 + [_vp, _i64] + [_vp]),
     "fbob_bob": (_i, _SIZES + [_vp] * 7 + [_vp] * 3 + [_vp] * 6 + [_vp]),

@@ -200,6 +200,52 @@ int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64
   return finish(fbob::launch_forward(c.p, a, static_cast<hipStream_t>(stream)));
 }
 
+int fbob_forward_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                int64_t d, float tau, int causal, int64_t* bytes) {
+  if (bytes == nullptr) return FBOB_ERR_INVALID_ARG;
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  *bytes = c.empty ? 0 : fbob::fwd_split_plan(c.p).bytes;
+  return FBOB_OK;
+}
+
+int fbob_forward_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    float tau, int causal, const void* Q, const void* K, const void* V,
+                    const void* dO, float* O, float* L, float* D, void* workspace,
+                    int64_t workspace_bytes, void* stream) {
+  Checked c = check_sizes(dtype, B, Hq, Hkv, N, d, tau, causal);
+  if (c.status != FBOB_OK) return c.status;
+  if (workspace_bytes < 0) return FBOB_ERR_INVALID_ARG;
+  if (c.empty) return FBOB_OK;
+  if ((dO == nullptr) != (D == nullptr)) return FBOB_ERR_INVALID_ARG;
+  const fbob::FwdPlan plan = fbob::fwd_split_plan(c.p);
+  // the split schedule only with a workspace that holds its partial states
+  const bool split = plan.bytes > 0 && workspace != nullptr && workspace_bytes >= plan.bytes;
+  const bool with_d = dO != nullptr;
+  const int64_t es = c.p.bf16 ? 2 : 4;
+  const int64_t qb = B * Hq * N * d * es, kb = B * Hkv * N * d * es;
+  const int64_t ob = B * Hq * N * d * 4, rb = B * Hq * N * 4;
+  const void* ins[] = {Q, K, V, dO};
+  const int64_t inb[] = {qb, kb, kb, qb};
+  void* outs[] = {O, L, with_d ? D : nullptr, split ? workspace : nullptr};
+  const int64_t outb[] = {ob, rb, rb, plan.bytes};
+  void* outs_c[4];
+  int64_t outb_c[4];
+  int n_out = 0;
+  for (int i = 0; i < 4; ++i)
+    if (outs[i] != nullptr || i < 2) {
+      outs_c[n_out] = outs[i];
+      outb_c[n_out++] = outb[i];
+    }
+  const int st = check_ptrs(ins, inb, with_d ? 4 : 3, outs_c, outb_c, n_out);
+  if (st != FBOB_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  fbob::FwdArgs a{Q, K, V, dO, O, L, D};
+  clear_pending();
+  if (split) return finish(fbob::launch_forward_split_all(c.p, a, plan, workspace, s));
+  return finish(fbob::launch_forward(c.p, a, s));
+}
+
 int fbob_bob_pass1(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float tau,
                    int causal, const void* Q, const void* K, const void* V, const void* dO,
                    const void* UQ, const void* UK, const void* UV, const float* O, const float* L,

@@ -39,6 +39,10 @@ struct Problem {
 struct FwdArgs {
   const void *Q, *K, *V, *dO;  // dO may be NULL: then D is not written
   float *O, *L, *D;
+  // Split key sweep (small grids): part[s][B Hq][N][d] holds split s's unnormalised O,
+  // part_ml[s][B Hq][N][2] its reference maximum (log2 units) and row sum.
+  float *part = nullptr, *part_ml = nullptr;
+  int nsplit = 1;
 };
 
 struct Pass1Args {
@@ -92,6 +96,16 @@ struct GradArgs {
 };
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
+// Split form (a.part, a.part_ml, a.nsplit set; bf16 only), its plan (parts, workspace
+// bytes; 1 / 0 = no split) and the split forward with its reduction.
+hipError_t launch_forward_split(const Problem& p, const FwdArgs& a, hipStream_t s);
+struct FwdPlan {
+  int s = 1;
+  int64_t bytes = 0;
+};
+FwdPlan fwd_split_plan(const Problem& p);
+hipError_t launch_forward_split_all(const Problem& p, const FwdArgs& a, const FwdPlan& plan,
+                                    void* workspace, hipStream_t s);
 hipError_t launch_pass1(const Problem& p, const Pass1Args& a, hipStream_t s);
 // The partial-sum forms (a.nsplit > 1) of the default Pass 1 / Pass 2 variants.
 hipError_t launch_pass1_split(const Problem& p, const Pass1Args& a, hipStream_t s);

@@ -93,6 +93,37 @@ int fbob_forward(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64
                  float* O, float* L, float* D, void* stream);
 
 /*
+ * Device workspace, in bytes, that fbob_forward_ws can use for this problem (0 when the
+ * row tiles fill the GPU, or the inputs are fp32: then fbob_forward_ws is fbob_forward).
+ * Same size arguments as fbob_forward; writes the size to *bytes.  FBOB_ERR_INVALID_ARG
+ * if bytes is NULL; size errors as fbob_forward.  No HIP call.
+ */
+int fbob_forward_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                int64_t d, float tau, int causal, int64_t* bytes);
+
+/*
+ * fbob_forward with a caller-owned device workspace for problems too small to fill the
+ * GPU: a work-group owns 256 query rows; when there are fewer of them than the resident
+ * work-group slots (512 at d = 64, 256 at d = 128), each row tile's key sweep is split
+ * over 2-16 work-groups.  Each keeps the online-softmax state of its keys (unnormalised
+ * O, row sum, reference maximum) in fp32 in the workspace, and a reduction merges the
+ * parts in a fixed order (FlashAttention blog, section 一: the softmax of a concatenation
+ * from the blocks' maxima and sums) and writes O, L and D once.  Deterministic; the
+ * results differ from fbob_forward's only by fp32 rounding order.  bf16 inputs.
+ *   workspace       DEVICE pointer, 16-byte aligned, owned by the caller, at least
+ *                   fbob_forward_workspace_size() bytes; NULL (or fewer bytes) runs
+ *                   exactly fbob_forward.  Contents on entry ignored, on return
+ *                   undefined; must not overlap any other argument (FBOB_ERR_ALIAS).
+ *                   Calls sharing one workspace must be ordered (same stream).
+ * Other arguments, outputs and errors as fbob_forward.
+ */
+int fbob_forward_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                    float tau, int causal,
+                    const void* Q, const void* K, const void* V, const void* dO,
+                    float* O, float* L, float* D,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * First-order attention backward (FlashAttention blog, "FlashAttention 的反向传播
  * 设计", section 一 for dV = P^T dO, dS = P o (dP - D), dQ = tau dS K,
  * dK = tau dS^T Q, and section 二 for rebuilding P on chip from L).  Two passes
@@ -245,7 +276,7 @@ int fbob_bob_ws(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_
  * device it runs on until the process ends; the library allocates nothing and
  * issues no memset (every partial a call reads is written earlier in that call).
  *   * FBOB_ERR_SCRATCH, before any HIP call, if the workspace size exceeds
- *     FBOB_SCRATCH_BYTES (e.g. B=1 H=10 N=4096 d=128 needs 160 MiB); fbob_bob or
+ *     FBOB_SCRATCH_BYTES (e.g. B=2 H=10 N=4096 d=128 needs 160 MiB); fbob_bob or
  *     fbob_bob_ws serve such problems.
  *   * All calls on one device share that device's array: calls that overlap in
  *     time on one device (on different streams, or from threads without an order

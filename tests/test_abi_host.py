@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
-        ["fbob_forward", "fbob_backward", "fbob_backward_ws", "fbob_backward_workspace_size",
+        ["fbob_forward", "fbob_forward_ws", "fbob_forward_workspace_size", "fbob_backward", "fbob_backward_ws", "fbob_backward_workspace_size",
          "fbob_bob", "fbob_bob_pass1", "fbob_bob_pass2",
          "fbob_bob_workspace_size", "fbob_bob_ws", "fbob_bob_ex", "fbob_bob_noalloc",
          "fbob_strerror", "fbob_hip_error_string", "fbob_version"])
@@ -334,6 +334,59 @@ def test_backward_workspace_size_and_validation(lib):
     bad = list(ptrs)
     bad[2] = ctypes.c_void_p(0)
     assert call(fb[10], need, p=bad) == INVALID
+
+
+def test_forward_workspace_size_and_validation(lib):
+    """fbob_forward_workspace_size follows the split forward's plan: with the mask, parts =
+    resident work-group slots (512 at d = 64, 256 at d = 128) over the 256-row tiles;
+    without it, the part count of least estimated time (whole CU rounds x stages per part
+    + the merge's traffic + a fixed cost) if that is at most 0.9 of the unsplit one; at
+    most a quarter of the key stages (of the mean causal sweep) and 16; s (d + 2) fp32 per
+    row.  Problems that fill the slots, fp32 ones and short sweeps need none; validation
+    as fbob_forward, plus the workspace's own."""
+    def fws(dtype=1, B=1, Hq=12, Hkv=12, N=4096, d=64, causal=0):
+        out = ctypes.c_int64(-1)
+        st = lib.fbob_forward_workspace_size(dtype, B, Hq, Hkv, N, d, ctypes.c_float(0.125),
+                                             causal, ctypes.byref(out))
+        return st, out.value
+    rows = 12 * 4096
+    assert fws() == (OK, 0)                            # 192 tiles: no split pays
+    assert fws(causal=1) == (OK, 3 * rows * 66 * 4)    # mean sweep 16 stages
+    assert fws(d=128) == (OK, 0)
+    assert fws(Hq=2, Hkv=2) == (OK, 8 * 2 * 4096 * 66 * 4)        # 32 tiles: 8 parts
+    assert fws(Hq=6, Hkv=6) == (OK, 2 * 6 * 4096 * 66 * 4)        # 96 tiles: one round
+    assert fws(Hq=6, Hkv=6, d=128) == (OK, 2 * 6 * 4096 * 130 * 4)
+    assert fws(Hq=2, Hkv=2, d=128) == (OK, 8 * 2 * 4096 * 130 * 4)
+    assert fws(Hq=12, Hkv=12, N=8192) == (OK, 2 * 12 * 8192 * 66 * 4)  # 384 tiles
+    assert fws(Hq=20, Hkv=20) == (OK, 0)
+    assert fws(Hq=1, Hkv=1, N=1024) == (OK, 2 * 1024 * 66 * 4)   # 8 stages: 2 parts
+    assert fws(Hq=1, Hkv=1, N=32768) == (OK, 2 * 32768 * 66 * 4)  # 128 tiles
+    assert fws(Hq=1, Hkv=1, N=65536) == (OK, 0)        # 256 tiles: one round either way
+    assert fws(Hq=1, Hkv=1, N=512) == (OK, 0)          # 4 stages: no split
+    assert fws(N=16384) == (OK, 0)                     # 768 tiles fill 512 slots
+    assert fws(dtype=0) == (OK, 0)
+    assert fws(N=0) == (OK, 0)
+    assert fws(d=96)[0] == UNSUPPORTED
+    assert lib.fbob_forward_workspace_size(1, 1, 1, 1, 64, 64, ctypes.c_float(0.125), 0,
+                                           None) == INVALID
+    fb = FakeBuffers(8)
+    ptrs = [fb[m] for m in range(7)]
+    need = fws(Hq=2, Hkv=2)[1]
+    assert need > 0
+
+    def call(ws, nbytes, p=ptrs, N=4096):
+        return lib.fbob_forward_ws(1, 1, 2, 2, N, 64, ctypes.c_float(0.125), 0, *p, ws,
+                                   nbytes, ctypes.c_void_p(0))
+    assert call(fb[7], -1) == INVALID
+    assert call(ctypes.c_void_p(fb.addrs[4] + 64), need) == ALIAS      # inside O
+    assert call(ctypes.c_void_p(fb.addrs[7] + 8), need) == ALIGN
+    assert call(fb[7], need, N=0) == OK
+    bad = list(ptrs)
+    bad[6] = ctypes.c_void_p(0)                                         # D NULL, dO given
+    assert call(fb[7], need, p=bad) == INVALID
+    bad = list(ptrs)
+    bad[1] = ctypes.c_void_p(0)
+    assert call(fb[7], need, p=bad) == INVALID
 
 
 def test_header_states_the_scratch_size():
