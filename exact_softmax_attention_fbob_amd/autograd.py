@@ -4,7 +4,8 @@
     O = attention(Q, K, V, tau=None, causal=False)      # O in Q's dtype
     O = attention(Q, K, V, fp32_row_sums=True)           # BoB with fp32 alpha, E'
 
-* forward: ``fbob_forward`` without dO (O and the log-partition L);
+* forward: ``fbob_forward_ws`` without dO (O and the log-partition L; a workspace from
+  torch's allocator, so that small problems split their key sweeps);
 * first backward (dQ, dK, dV for an upstream dO): ``fbob_backward_ws`` (a workspace
   from torch's allocator, so that small problems split their sweeps), which also
   returns the row scalar D;
@@ -40,7 +41,7 @@ import torch
 from . import FLAG_FP32_ROW_SUMS as _FLAG_FP32_ROW_SUMS
 from . import backward_ws as _backward
 from . import bob_ex as _bob_ex
-from . import forward as _forward
+from . import forward_ws as _forward
 
 __all__ = ["attention"]
 

@@ -2,7 +2,7 @@
 length (tiny, ragged, several tiles), head size, mask, tau, input scale and storage
 type that the hand-picked cases do not cover one by one.  A second, wider draw of 150
 runs every BoB entry point (the fp32 row-sum option and the static-scratch form too) and
-the first backward's split form.
+the forward's and the first backward's split forms.
 
 Every configuration runs the forward, the BoB (``fbob_bob``, and ``fbob_bob_ws`` with
 the workspace the planner asks for) and the first backward through the C ABI and
@@ -134,8 +134,8 @@ def test_random_configuration_matches_oracle(w):
 @pytest.mark.parametrize("w", WIDE, ids=[w.name for w in WIDE])
 def test_wide_random_configuration_every_bob_entry_point(w):
     """fbob_bob, fbob_bob_ws, fbob_bob_ex with fp32 row sums and fbob_bob_noalloc (where
-    the split fits the static scratch), and the first backward through fbob_backward_ws,
-    against the oracle, every output element."""
+    the split fits the static scratch), the forward through fbob_forward_ws and the first
+    backward through fbob_backward_ws, against the oracle, every output element."""
     import torch
     import exact_softmax_attention_fbob_amd as fb
     U.say(f"[wide] {w.name}")
@@ -157,6 +157,12 @@ def test_wide_random_configuration_every_bob_entry_point(w):
                    D=D.cpu().numpy().astype(np.float64))
         keys = U.ALL_KEYS + (("O", "L", "D") if kind == "bob" else ())
         errs.update({f"{kind}.{k}": v for k, v in U.compare_full(got, ref, w, keys=keys).items()})
+    # the forward through fbob_forward_ws (split where its planner splits)
+    fO, fL, fD = fb.forward_ws(*a7[:4], w.tau, w.causal)
+    fgot = {"O": fO.cpu().numpy().astype(np.float64), "L": fL.cpu().numpy().astype(np.float64),
+            "D": fD.cpu().numpy().astype(np.float64)}
+    errs.update({f"fwd_ws.{k}": v
+                 for k, v in U.compare_full(fgot, ref, w, keys=("O", "L", "D")).items()})
     # the first backward through fbob_backward_ws (split where its planner splits)
     g = fb.backward_ws(*a7[:4], O, L, w.tau, w.causal)
     gd = {kk: v.cpu().numpy().astype(np.float64) for kk, v in g.items()}
